@@ -1,0 +1,124 @@
+"""Seeded synthetic inputs for the attention forward/backward workloads.
+
+Shared by the tests, the benchmark and the smoke check; used on both sides
+of every parity comparison (the oracle gets the exact fp64 upcast of the
+same bf16 values the GPU gets).  This module holds no attention arithmetic:
+only random draws, the fixed input constructions below, and round-to-
+nearest-even conversion to bf16.
+
+Recipe (the pages measure on no public dataset; these stand in for the
+unspecified FlashAttention-4 forward workload):
+  * numpy PCG64, ``default_rng(seed)``, ``standard_normal(dtype=float32)``,
+    drawn in the order Q, K, V, dO, each shaped [B,H,S,D];
+  * the "rescale stress" construction scales Q and K by 3, sets every
+    query's first feature to 4.0 and adds 0.002*j to key j's first feature,
+    so each row's running maximum keeps rising along the sequence;
+  * everything is rounded to bf16 (round to nearest, ties to even) once,
+    after construction.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+SEED_BASE = 20260000
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    S: int
+    D: int
+    causal: bool
+    stress: bool = False  # rising-maximum construction
+    backward: bool = False
+    index: int = 0
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.D)
+
+    @property
+    def seed(self) -> int:
+        return SEED_BASE + self.index
+
+    def describe(self) -> str:
+        return "B=%d H=%d S=%d D=%d %s%s%s" % (
+            self.B, self.H, self.S, self.D, "causal" if self.causal else "non-causal",
+            " rescale-stress" if self.stress else "", " backward" if self.backward else "")
+
+
+# The five workloads: a tiny one the oracle finishes instantly, a non-causal
+# S=2048 forward, two causal long-sequence forwards (one of them built so the
+# running maximum keeps rising), and a causal backward.
+WORKLOADS = {
+    "tiny": Workload("tiny", 1, 2, 128, 64, False, index=1),
+    "fwd_s2k": Workload("fwd_s2k", 4, 16, 2048, 128, False, index=2),
+    "fwd_causal_s8k": Workload("fwd_causal_s8k", 2, 32, 8192, 128, True, index=3),
+    "fwd_stress_s16k": Workload("fwd_stress_s16k", 1, 16, 16384, 128, True, stress=True, index=4),
+    "bwd_causal_s4k": Workload("bwd_causal_s4k", 2, 16, 4096, 128, True, backward=True, index=5),
+}
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp32 to bf16, nearest-even; returns the uint16 bit patterns."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    nan = np.isnan(x)
+    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    r = r.astype(np.uint16)
+    if nan.any():
+        r[nan] = 0x7FC0
+    return r
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Exact upcast of bf16 bit patterns to fp32."""
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def bf16_bits_to_f64(b: np.ndarray) -> np.ndarray:
+    """Exact upcast of bf16 bit patterns to fp64."""
+    return bf16_bits_to_f32(b).astype(np.float64)
+
+
+def make_inputs(B: int, H: int, S: int, D: int, seed: int, stress: bool = False,
+                with_dout: bool = False) -> dict:
+    """Draw Q, K, V (and dO) as bf16 bit arrays [B,H,S,D] (uint16)."""
+    rng = np.random.default_rng(seed)
+    shape = (B, H, S, D)
+    q = rng.standard_normal(shape, dtype=np.float32)
+    k = rng.standard_normal(shape, dtype=np.float32)
+    v = rng.standard_normal(shape, dtype=np.float32)
+    if stress:
+        q *= np.float32(3.0)
+        k *= np.float32(3.0)
+        q[..., 0] = np.float32(4.0)
+        k[..., 0] += (np.float32(0.002) * np.arange(S, dtype=np.float32))[None, None, :]
+    out = {"q": f32_to_bf16_bits(q), "k": f32_to_bf16_bits(k), "v": f32_to_bf16_bits(v)}
+    del q, k, v
+    if with_dout:
+        out["do"] = f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32))
+    return out
+
+
+def workload_inputs(w: Workload) -> dict:
+    return make_inputs(w.B, w.H, w.S, w.D, w.seed, stress=w.stress, with_dout=w.backward)
+
+
+def to_torch_bf16(bits: np.ndarray, device=None):
+    """View uint16 bf16 bit patterns as a torch.bfloat16 tensor (copied to device)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16)
+    return t.to(device) if device is not None else t
+
+
+def torch_bf16_to_bits(t) -> np.ndarray:
+    """Bit patterns of a torch.bfloat16 tensor as a uint16 numpy array."""
+    import torch
+    return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
