@@ -1,0 +1,212 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused exact-attention hot path on one MI355X.
+
+One step = the whole path over one batch of seeded synthetic input: the fused
+forward (O, LSE) followed by the backward (Delta, dK/dV with dQ accumulation,
+dQ cast) that consumes the forward's O and LSE.  The default workload is the
+causal backward workload (B=2, H=16, S=4096, D=128, bf16), the one workload
+that exercises every step.  Throughput is algorithmic TFLOPS: forward
+4*B*H*S^2*D (halved when causal) plus backward 2.5x that.
+
+Also measured, in the same process:
+  * the dominant kernel (the backward main kernel) on its own, timed with HIP
+    events on the stream it is launched on -> "roofline" (MFMA bound);
+  * the forward alone on the three forward workloads (S=2048 non-causal, S=8192
+    causal, S=16384 causal rising-maximum) -> "legs" and "fwd_roofline";
+  * the fp64 CPU oracle on a bounded sample of the same workload on this host's
+    cores -> "cpu_baseline" (a reported baseline, not the target).
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def fwd_flops(B, H, S, D, causal):
+    f = 4.0 * B * H * S * S * D
+    return f / 2 if causal else f
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="bwd_causal_s4k")
+    ap.add_argument("--no-legs", action="store_true", help="skip the forward-only legs")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time for the oracle sample")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library's path has no multi-GPU "
+              "step (independent heads shard with no exchange); run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import attn_inputs as ai
+    import exact_attention_128_amd as A
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    w = ai.WORKLOADS[args.workload]
+    B, H, S, D, causal, scale = w.B, w.H, w.S, w.D, w.causal, w.scale
+    log("workload", w.name, w.describe())
+
+    bits = ai.make_inputs(B, H, S, D, w.seed, stress=w.stress, with_dout=True)
+    q, k, v, do = (ai.to_torch_bf16(bits[n], dev) for n in ("q", "k", "v", "do"))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws = torch.empty(A.bwd_workspace_size(B, H, S, D), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        A.fwd_out(q, k, v, o, lse, causal=causal, scale=scale)
+        A.bwd_out(q, k, v, o, lse, do, dq, dk, dv, ws, causal=causal, scale=scale)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_step = e0.elapsed_time(e1) / args.steps
+    f_fwd = fwd_flops(B, H, S, D, causal)
+    f_bwd = 2.5 * f_fwd
+    value = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
+    log("step: %.3f ms  %.1f TFLOPS (wall %.3f ms/step)" % (ms_step, value,
+                                                          1e3 * t_wall / args.steps))
+
+    def time_launches(fn, n):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(n):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    # dominant kernel: backward main (run PRE once so the workspace holds Delta)
+    A.bwd_out(q, k, v, o, lse, do, dq, dk, dv, ws, causal=causal, scale=scale, phases=A.BWD_PRE)
+    n_rep = max(args.steps, 10)
+    ms_main = time_launches(lambda: A.bwd_out(q, k, v, o, lse, do, dq, dk, dv, ws, causal=causal,
+                                              scale=scale, phases=A.BWD_MAIN), n_rep)
+    ms_fwd = time_launches(lambda: A.fwd_out(q, k, v, o, lse, causal=causal, scale=scale), n_rep)
+    ms_bwd = time_launches(lambda: A.bwd_out(q, k, v, o, lse, do, dq, dk, dv, ws, causal=causal,
+                                             scale=scale), n_rep)
+    main_tflops = f_bwd / (ms_main * 1e-3) / 1e12
+    log("bwd main %.3f ms (%.1f TFLOPS), fwd %.3f ms, bwd total %.3f ms" % (
+        ms_main, main_tflops, ms_fwd, ms_bwd))
+
+    legs = {}
+    fwd_roof = None
+    if not args.no_legs:
+        del q, k, v, do, o, lse, dq, dk, dv, ws
+        torch.cuda.empty_cache()
+        for name in ("fwd_s2k", "fwd_causal_s8k", "fwd_stress_s16k"):
+            lw = ai.WORKLOADS[name]
+            lb = ai.workload_inputs(lw)
+            lq, lk, lv = (ai.to_torch_bf16(lb[n], dev) for n in ("q", "k", "v"))
+            lo = torch.empty_like(lq)
+            ll = torch.empty((lw.B, lw.H, lw.S), dtype=torch.float32, device=dev)
+            for _ in range(3):
+                A.fwd_out(lq, lk, lv, lo, ll, causal=lw.causal, scale=lw.scale)
+            ms = time_launches(lambda: A.fwd_out(lq, lk, lv, lo, ll, causal=lw.causal,
+                                                 scale=lw.scale), n_rep)
+            fl = fwd_flops(lw.B, lw.H, lw.S, lw.D, lw.causal)
+            tf = fl / (ms * 1e-3) / 1e12
+            legs[name] = {"shape": [lw.B, lw.H, lw.S, lw.D], "causal": lw.causal,
+                          "ms": round(ms, 4), "tflops": round(tf, 1),
+                          "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+            log("fwd leg %s: %.3f ms  %.1f TFLOPS (%.1f%%)" % (name, ms, tf,
+                                                               100 * tf / PEAK_BF16_TFLOPS))
+            del lq, lk, lv, lo, ll
+            torch.cuda.empty_cache()
+        c3 = legs["fwd_causal_s8k"]
+        fwd_roof = {"kernel": "attn_fwd_kernel<128,causal>", "workload": "fwd_causal_s8k",
+                    "bound": "mfma", "achieved": c3["tflops"], "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": c3["frac_peak"], "traffic": None}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        try:
+            cores = len(os.sched_getaffinity(0))
+        except AttributeError:
+            cores = os.cpu_count() or 1
+        cores = min(cores, int(os.environ.get("OMP_NUM_THREADS", cores)))
+        oracle.set_threads(cores)
+        qs, ks, vs, dos = (bits[n].reshape(B * H, S, D) for n in ("q", "k", "v", "do"))
+        t0 = time.perf_counter()
+        heads = 0
+        while heads < B * H and time.perf_counter() - t0 < args.cpu_seconds:
+            oracle.attn_bwd_head(*(ai.bf16_bits_to_f64(x[heads]) for x in (qs, ks, vs, dos)),
+                                 scale, causal)
+            heads += 1
+        dt = time.perf_counter() - t0
+        per_head = (f_fwd + f_bwd) / (B * H)
+        cpu = {"value": round(heads * per_head / dt / 1e12, 6), "unit": "TFLOPS",
+               "cores": oracle.max_threads(), "kind": "oracle",
+               "sample": "%d of %d heads of the workload, fp64 forward+backward per head, "
+                         "%.1f s" % (heads, B * H, dt)}
+        log("cpu oracle: %s" % cpu)
+
+    out = {
+        "metric": "attention fwd/bwd TFLOPS (bf16, D=128) and % of MI355X bf16 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 inputs, seed %d)" % w.seed,
+        "config": {"workload": w.name, "B": B, "H": H, "S": S, "D": D, "causal": causal,
+                   "step": "forward + backward", "frac_peak": round(value / PEAK_BF16_TFLOPS, 4)},
+        "roofline": {"kernel": "attn_bwd_main_kernel<128,causal>", "bound": "mfma",
+                     "achieved": round(main_tflops, 1), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(main_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+        "fwd_ms": round(ms_fwd, 4),
+        "bwd_ms": round(ms_bwd, 4),
+        "fwd_tflops": round(f_fwd / (ms_fwd * 1e-3) / 1e12, 1),
+        "bwd_tflops": round(f_bwd / (ms_bwd * 1e-3) / 1e12, 1),
+        "fwd_roofline": fwd_roof,
+        "legs": legs,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,122 @@
+"""Fused exact attention for AMD MI355X (gfx950): thin Python binding.
+
+Every step of the computation runs in the HIP kernels of ``libattn.so``
+(built from ``csrc/`` by ``build.py``); this module only checks tensors,
+allocates outputs with PyTorch and passes raw device pointers and the current
+stream through the C ABI declared in ``include/attn.h``.  There is no CPU or
+PyTorch fallback: if the library is missing, every call raises.
+
+    o, lse = fwd(q, k, v, causal=False, scale=None)
+    dq, dk, dv = bwd(q, k, v, o, lse, do, causal=False, scale=None)
+
+q, k, v, do: torch.bfloat16 CUDA tensors, contiguous [B, H, S, D], D in {64, 128}.
+"""
+from __future__ import annotations
+
+import math
+
+from . import _lib
+from ._lib import AttnError, load, library_path  # noqa: F401
+
+__all__ = ["fwd", "bwd", "fwd_out", "bwd_out", "bwd_workspace_size", "AttnError", "load",
+           "library_path"]
+
+
+def _check(t, name, shape=None):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.dtype != torch.bfloat16:
+        raise TypeError("%s must be torch.bfloat16, got %s" % (name, t.dtype))
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on a GPU device" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous [B,H,S,D]" % name)
+    if t.dim() != 4:
+        raise ValueError("%s must be 4-D [B,H,S,D]" % name)
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s shape %s != %s" % (name, tuple(t.shape), tuple(shape)))
+
+
+def _stream(device):
+    import torch
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def fwd_out(q, k, v, o, lse, causal: bool = False, scale: float | None = None,
+            rescale_log2: float | None = None) -> None:
+    """Forward into caller-provided o (bf16 [B,H,S,D]) and lse (fp32 [B,H,S])."""
+    import torch
+    _check(q, "q")
+    B, H, S, D = q.shape
+    _check(k, "k", q.shape)
+    _check(v, "v", q.shape)
+    _check(o, "o", q.shape)
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, S) or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [B,H,S]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    st = _stream(q.device)
+    if rescale_log2 is None:
+        rc = _lib.load().attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                  lse.data_ptr(), B, H, S, D, float(scale), int(bool(causal)), st)
+    else:
+        rc = _lib.load().attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                     lse.data_ptr(), B, H, S, D, float(scale), int(bool(causal)),
+                                     float(rescale_log2), st)
+    _lib.raise_for(rc, "attn_fwd")
+
+
+def fwd(q, k, v, causal: bool = False, scale: float | None = None,
+        rescale_log2: float | None = None):
+    """Returns (O bf16 [B,H,S,D], LSE fp32 [B,H,S])."""
+    import torch
+    _check(q, "q")
+    B, H, S, D = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    fwd_out(q, k, v, o, lse, causal=causal, scale=scale, rescale_log2=rescale_log2)
+    return o, lse
+
+
+def bwd_workspace_size(B: int, H: int, S: int, D: int) -> int:
+    return int(_lib.load().attn_bwd_workspace_size(B, H, S, D))
+
+
+BWD_PRE, BWD_MAIN, BWD_CAST, BWD_ALL = 1, 2, 4, 7
+
+
+def bwd_out(q, k, v, o, lse, do, dq, dk, dv, workspace, causal: bool = False,
+            scale: float | None = None, phases: int = BWD_ALL) -> None:
+    """Backward into caller-provided dq, dk, dv and a uint8 workspace tensor.
+
+    `phases` selects a subset of the three launches (see attn_bwd_phases)."""
+    import torch
+    _check(q, "q")
+    B, H, S, D = q.shape
+    for name, t in (("k", k), ("v", v), ("o", o), ("do", do), ("dq", dq), ("dk", dk), ("dv", dv)):
+        _check(t, name, q.shape)
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, S) or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [B,H,S]")
+    if workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on q's device")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    nbytes = workspace.numel() * workspace.element_size()
+    rc = _lib.load().attn_bwd_phases(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                     lse.data_ptr(), do.data_ptr(), dq.data_ptr(),
+                                     dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), nbytes,
+                                     B, H, S, D, float(scale), int(bool(causal)), int(phases),
+                                     _stream(q.device))
+    _lib.raise_for(rc, "attn_bwd")
+
+
+def bwd(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None):
+    """Returns (dQ, dK, dV), bf16 [B,H,S,D]."""
+    import torch
+    _check(q, "q")
+    B, H, S, D = q.shape
+    ws = torch.empty(max(1, bwd_workspace_size(B, H, S, D)), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    bwd_out(q, k, v, o, lse, do, dq, dk, dv, ws, causal=causal, scale=scale)
+    return dq, dk, dv

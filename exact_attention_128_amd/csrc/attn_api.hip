@@ -1,0 +1,154 @@
+// attn_api.hip -- the C ABI declared in include/attn.h: host-side argument
+// validation, scale handling, workspace layout and dispatch to the kernels.
+// Every check runs before the first HIP call, so invalid requests never touch
+// the device.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/attn.h"
+#include "attn_internal.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+
+int check_shape(int B, int H, int S, int D) {
+  if (B < 1 || H < 1 || S < 1) return ATTN_ERR_SHAPE;
+  if (D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
+  const int64_t bh = int64_t(B) * H;
+  if (bh > 0x7fffffffLL) return ATTN_ERR_SHAPE;
+  if (bh * S * D >= kMaxElems) return ATTN_ERR_SHAPE;
+  return ATTN_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return ATTN_OK;
+  g_last_hip_error = static_cast<int>(e);
+  return ATTN_ERR_HIP;
+}
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+             int S, int D, float scale, int causal, float tau, attn_stream_t stream) {
+  if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
+  int rc = check_shape(B, H, S, D);
+  if (rc) return rc;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(lse, 4))
+    return ATTN_ERR_ALIGN;
+  if (!isfinite(scale)) return ATTN_ERR_SCALE;
+  if (!(tau >= 0.0f && tau <= 64.0f)) return ATTN_ERR_SCALE;
+
+  attn::FwdParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<uint16_t*>(o);
+  p.lse = lse;
+  p.bh = B * H;
+  p.S = S;
+  // softmax(scale * q.k) == softmax(|scale| * (-q).k): negate Q (exact in
+  // bf16) for a negative scale so the kernels always see c > 0; a zero scale
+  // gives uniform weights, the same as zeroing Q.
+  p.qand = 0xffffffffu;
+  p.qxor = 0u;
+  if (scale < 0.0f) p.qxor = 0x80008000u;
+  if (scale == 0.0f) p.qand = 0u;
+  p.c = (scale == 0.0f) ? 1.0f : fabsf(scale) * attn::kLog2eHost;
+  p.tau = tau;
+  return hip_status(attn::launch_fwd(p, D, causal != 0, reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+             int S, int D, float scale, int causal, attn_stream_t stream) {
+  return fwd_impl(q, k, v, o, lse, B, H, S, D, scale, causal, 8.0f, stream);
+}
+
+int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                int S, int D, float scale, int causal, float rescale_log2,
+                attn_stream_t stream) {
+  return fwd_impl(q, k, v, o, lse, B, H, S, D, scale, causal, rescale_log2, stream);
+}
+
+size_t attn_bwd_workspace_size(int B, int H, int S, int D) {
+  if (check_shape(B, H, S, D) != ATTN_OK) return 0;
+  const size_t rows = size_t(B) * H * S;
+  return round_up(rows * sizeof(float), 256) + round_up(rows * D * sizeof(float), 256);
+}
+
+int attn_bwd_phases(const void* q, const void* k, const void* v, const void* o,
+                    const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                    void* workspace, size_t workspace_bytes, int B, int H, int S, int D,
+                    float scale, int causal, unsigned phases, attn_stream_t stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !workspace)
+    return ATTN_ERR_NULL;
+  int rc = check_shape(B, H, S, D);
+  if (rc) return rc;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
+      !aligned(lse, 4) || !aligned(workspace, 256))
+    return ATTN_ERR_ALIGN;
+  if (!isfinite(scale)) return ATTN_ERR_SCALE;
+  if (workspace_bytes < attn_bwd_workspace_size(B, H, S, D)) return ATTN_ERR_WORKSPACE;
+
+  const size_t rows = size_t(B) * H * S;
+  attn::BwdParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<const uint16_t*>(o);
+  p.lse = lse;
+  p.dout = static_cast<const uint16_t*>(dout);
+  p.dq = static_cast<uint16_t*>(dq);
+  p.dk = static_cast<uint16_t*>(dk);
+  p.dv = static_cast<uint16_t*>(dv);
+  p.delta = static_cast<float*>(workspace);
+  p.dqacc = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                     round_up(rows * sizeof(float), 256));
+  p.bh = B * H;
+  p.S = S;
+  p.scale = scale;
+  p.c = scale * attn::kLog2eHost;
+  if (phases == 0 || (phases & ~unsigned(ATTN_BWD_ALL)) != 0) return ATTN_ERR_UNSUPPORTED;
+  return hip_status(
+      attn::launch_bwd(p, D, causal != 0, phases, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+             const void* dout, void* dq, void* dk, void* dv, void* workspace,
+             size_t workspace_bytes, int B, int H, int S, int D, float scale, int causal,
+             attn_stream_t stream) {
+  return attn_bwd_phases(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, H, S,
+                         D, scale, causal, ATTN_BWD_ALL, stream);
+}
+
+const char* attn_strerror(int status) {
+  switch (status) {
+    case ATTN_OK: return "success";
+    case ATTN_ERR_NULL: return "a required pointer is NULL";
+    case ATTN_ERR_SHAPE: return "invalid shape: B, H and S must be >= 1 and B*H*S*D < 2^40";
+    case ATTN_ERR_HEAD_DIM: return "unsupported head dimension: D must be 64 or 128";
+    case ATTN_ERR_ALIGN:
+      return "misaligned pointer: bf16 tensors need 16 bytes, LSE 4, workspace 256";
+    case ATTN_ERR_WORKSPACE: return "workspace smaller than attn_bwd_workspace_size()";
+    case ATTN_ERR_SCALE: return "scale not finite, or rescale threshold outside [0, 64]";
+    case ATTN_ERR_UNSUPPORTED: return "request not supported by this build";
+    case ATTN_ERR_HIP: return "HIP runtime error (see attn_last_hip_error)";
+    default: return "unknown status code";
+  }
+}
+
+int attn_last_hip_error(void) { return g_last_hip_error; }
+
+int attn_version(void) { return 100; }
+
+}  // extern "C"

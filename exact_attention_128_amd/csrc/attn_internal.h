@@ -1,0 +1,51 @@
+// attn_internal.h -- launch descriptors shared by the host entry points and
+// the kernel translation units (not part of the public ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+constexpr float kLog2eHost = 1.4426950408889634f;
+
+// One forward launch.  Tensors are [B*H][S][D] bf16 (raw 16-bit words).
+struct FwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  int bh;         // B * H
+  int S;          // sequence length (queries = keys)
+  int nqb;        // query blocks per head
+  float c;        // |scale| * log2(e), or 1 when scale == 0 (always > 0)
+  uint32_t qxor;  // applied to every Q word pair: 0 (scale > 0) or 0x80008000 (scale < 0)
+  uint32_t qand;  // 0xffffffff, or 0 when scale == 0 (Q treated as zero)
+  float tau;      // rescale threshold in log2 units
+  int xcd_heads;  // heads per XCD for the XCD-aware block order, 0 = plain order
+};
+
+// One backward launch.
+struct BwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const float* lse;
+  const uint16_t* dout;
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  float* delta;   // [B*H][S] fp32 workspace
+  float* dqacc;   // [B*H][S][D] fp32 workspace
+  int bh;
+  int S;
+  float scale;    // the logit scale (any finite value)
+  float c;        // scale * log2(e)
+};
+
+hipError_t launch_fwd(const FwdParams& p, int D, bool causal, hipStream_t stream);
+hipError_t launch_bwd(const BwdParams& p, int D, bool causal, unsigned phases, hipStream_t stream);
+
+}  // namespace attn

@@ -1,0 +1,154 @@
+/*
+ * attn.h -- C ABI of the fused exact-attention library for AMD MI355X (gfx950).
+ *
+ * The operation.  Exact scaled-dot-product attention, the computation that the
+ * FlashAttention-4 pages are about ("英伟达最强B200算力浪费60%", QbitAI; and the
+ * Tencent Cloud article "AI Infra 系列 第六章 GPU 性能工程（二）", section 7, FA4's
+ * four techniques).  Per (batch b, head h) and query row i:
+ *
+ *     s_ij  = scale * sum_d Q[b,h,i,d] * K[b,h,j,d]      for visible keys j
+ *     O_i   = sum_j softmax_j(s_ij) * V[b,h,j,:]
+ *     LSE_i = ln sum_j exp(s_ij)                          (natural log)
+ *
+ * Visible keys: every j in [0, S), or only j <= i when `causal` is nonzero.  The
+ * S x S score matrix never reaches memory: it is built tile by tile on chip with
+ * an online softmax (the pages: section 7 of the Tencent Cloud article, and
+ * section 5's tiling/fusion levers).  The backward computes dQ, dK, dV of the
+ * same function, recomputing the probabilities from LSE instead of storing
+ * them (section 5's recomputation lever).
+ *
+ * Conventions shared by every entry point.
+ *   - Tensors are contiguous, row-major [B][H][S][D]: element (b,h,i,d) sits at
+ *     ((b*H + h)*S + i)*D + d.  Q, K, V, O, dO, dQ, dK, dV are bf16 (16-bit
+ *     brain float, passed as raw 16-bit words); LSE is fp32 [B][H][S].
+ *   - All tensor pointers are DEVICE pointers on the current HIP device, owned
+ *     by the caller.  The library allocates no device memory and keeps no device
+ *     state; the backward's scratch space is a caller-provided workspace.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *     the call returns without synchronising.  Errors raised while the kernels
+ *     run surface at the caller's next synchronisation on that stream.
+ *   - Arguments are validated on the host before any HIP call.  No C++
+ *     exception crosses this boundary.  Calls are thread-safe and re-entrant.
+ *   - Supported: B, H, S >= 1 (any S; partial tiles are masked), D in {64, 128},
+ *     B*H*S*D < 2^40 elements, any finite scale.
+ *   - Arithmetic: bf16 inputs, fp32 accumulation in the matrix cores, fp32
+ *     softmax statistics, outputs rounded to nearest-even.
+ */
+#ifndef EXACT_ATTN_H
+#define EXACT_ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as hipStream_t (HIP's stream handle), without needing HIP headers. */
+typedef struct ihipStream_t* attn_stream_t;
+
+/* Status codes returned by every entry point. */
+enum attn_status {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = 1,        /* a required pointer is NULL                         */
+  ATTN_ERR_SHAPE = 2,       /* B, H or S < 1, or B*H*S*D >= 2^40                  */
+  ATTN_ERR_HEAD_DIM = 3,    /* D is not 64 or 128                                 */
+  ATTN_ERR_ALIGN = 4,       /* a bf16 tensor not 16-byte aligned, LSE not 4-byte,
+                               or the workspace not 256-byte aligned              */
+  ATTN_ERR_WORKSPACE = 5,   /* workspace smaller than attn_bwd_workspace_size()   */
+  ATTN_ERR_SCALE = 6,       /* scale (or a rescale threshold) not finite / in range */
+  ATTN_ERR_UNSUPPORTED = 7, /* a valid request this build does not implement      */
+  ATTN_ERR_HIP = 8          /* the HIP runtime refused the launch; see
+                               attn_last_hip_error()                              */
+};
+
+/*
+ * Forward: O and LSE of exact attention (definition above).
+ *   q, k, v  [B][H][S][D] bf16, read only.
+ *   o        [B][H][S][D] bf16, written.  May not alias q, k or v.
+ *   lse      [B][H][S] fp32, written: the natural-log log-sum-exp of each
+ *            row's scaled, visible logits (what the backward consumes).
+ *   scale    multiplies the logits before masking and softmax (usually 1/sqrt(D)).
+ *   causal   nonzero: key j is visible to query i iff j <= i.
+ * The online softmax rescales the running output only when a row's maximum
+ * grows by more than 8 (log2 units) over the stale maximum it is using, the
+ * conditional-rescaling idea of FA4 (Tencent Cloud article, section 7); the
+ * result is the same, see attn_fwd_ex.
+ * Returns ATTN_OK or an attn_status code; nothing is written on error.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int H, int S, int D, float scale, int causal,
+             attn_stream_t stream);
+
+/*
+ * Forward with an explicit rescale threshold `rescale_log2` in [0, 64]:
+ * the running output of a row is rescaled only when the row maximum has grown
+ * by more than rescale_log2 (in units of log2) past the maximum in use;
+ * 0 rescales whenever the maximum grows.  Every threshold yields the same
+ * exact result up to rounding (the stale maximum cancels between numerator
+ * and denominator).  Other arguments as attn_fwd.  Out-of-range threshold:
+ * ATTN_ERR_SCALE.
+ */
+int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                int B, int H, int S, int D, float scale, int causal,
+                float rescale_log2, attn_stream_t stream);
+
+/*
+ * Bytes of device workspace attn_bwd needs for this shape (0 if the shape is
+ * invalid): an fp32 row statistic Delta_i = sum_d dO_id * O_id [B][H][S] and an
+ * fp32 dQ accumulator [B][H][S][D], each 256-byte aligned.
+ */
+size_t attn_bwd_workspace_size(int B, int H, int S, int D);
+
+/*
+ * Backward: gradients of sum(dO * O) for the forward above.
+ *   q, k, v      the forward's inputs (bf16 [B][H][S][D]).
+ *   o, lse       the forward's outputs (bf16 O, fp32 LSE) for the same inputs.
+ *   dout         dO, bf16 [B][H][S][D].
+ *   dq, dk, dv   bf16 [B][H][S][D], written.  Must not alias any input.
+ *   workspace    device memory of at least attn_bwd_workspace_size(B,H,S,D)
+ *                bytes, 256-byte aligned, owned by the caller; its contents
+ *                on entry do not matter and are garbage on return.
+ * dQ is accumulated with fp32 atomics, so its low bits may differ between
+ * runs; dK and dV are deterministic.  Enqueues three kernels on `stream`.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o,
+             const float* lse, const void* dout, void* dq, void* dk, void* dv,
+             void* workspace, size_t workspace_bytes, int B, int H, int S,
+             int D, float scale, int causal, attn_stream_t stream);
+
+/* Phases of the backward, for attn_bwd_phases. */
+enum attn_bwd_phase {
+  ATTN_BWD_PRE = 1,   /* Delta = rowsum(dO * O) into the workspace; zero the dQ accumulator */
+  ATTN_BWD_MAIN = 2,  /* dK, dV written; dQ accumulated into the workspace                  */
+  ATTN_BWD_CAST = 4,  /* dQ = bf16(scale * accumulator)                                     */
+  ATTN_BWD_ALL = 7
+};
+
+/*
+ * attn_bwd restricted to the phases set in `phases` (a nonzero subset of
+ * ATTN_BWD_ALL), enqueued in the order PRE, MAIN, CAST.  A phase reads what the
+ * earlier phases left in `workspace`, so running MAIN without a preceding PRE
+ * on the same workspace adds onto the previous accumulator.  For callers that
+ * time or schedule the phases separately; arguments otherwise as attn_bwd.
+ * phases == 0 or outside ATTN_BWD_ALL: ATTN_ERR_UNSUPPORTED.
+ */
+int attn_bwd_phases(const void* q, const void* k, const void* v, const void* o,
+                    const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                    void* workspace, size_t workspace_bytes, int B, int H, int S,
+                    int D, float scale, int causal, unsigned phases,
+                    attn_stream_t stream);
+
+/* Static English description of a status code (never NULL). */
+const char* attn_strerror(int status);
+
+/* Raw hipError_t of the last ATTN_ERR_HIP returned on the calling thread. */
+int attn_last_hip_error(void);
+
+/* Library ABI version: major*10000 + minor*100 + patch. */
+int attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXACT_ATTN_H */

@@ -1,0 +1,135 @@
+"""Helpers shared by the GPU parity tests: run the HIP path through the C ABI,
+run the fp64 oracle on the same bf16 inputs, and compare element by element.
+
+Tolerances (bf16 inputs, fp32 accumulation): O max |err| <= 2e-2 and mean
+|err| <= 2e-3, LSE max |err| <= 1e-3, dQ/dK/dV max |err| <= 5e-2.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import attn_inputs as ai
+import oracle
+
+O_MAX, O_MEAN, LSE_MAX, GRAD_MAX = 2e-2, 2e-3, 1e-3, 5e-2
+
+
+def gpu_fwd(bits, causal, scale, rescale_log2=None, stream=None):
+    """Run the forward on cuda:0; returns (O as fp64 numpy, LSE fp64 numpy, O bits)."""
+    import torch
+    import exact_attention_128_amd as A
+    dev = torch.device("cuda", 0)
+    q, k, v = (ai.to_torch_bf16(bits[n], dev) for n in ("q", "k", "v"))
+    if stream is None:
+        o, lse = A.fwd(q, k, v, causal=causal, scale=scale, rescale_log2=rescale_log2)
+    else:
+        with torch.cuda.stream(stream):
+            o, lse = A.fwd(q, k, v, causal=causal, scale=scale, rescale_log2=rescale_log2)
+        stream.synchronize()
+    torch.cuda.synchronize()
+    ob = ai.torch_bf16_to_bits(o)
+    return ai.bf16_bits_to_f64(ob), lse.cpu().numpy().astype(np.float64), ob
+
+
+def oracle_fwd_full(bits, causal, scale):
+    q, k, v = (ai.bf16_bits_to_f64(bits[n]) for n in ("q", "k", "v"))
+    return oracle.attn_fwd(q, k, v, scale, causal)
+
+
+def sample_rows(B, H, S, n_heads, n_rows, seed, block=128):
+    """Pick heads and rows: sequence start/end, tile and block edges, random rows."""
+    rng = np.random.default_rng(seed)
+    heads = sorted(set([0, B * H - 1] + list(rng.choice(B * H, size=min(n_heads, B * H),
+                                                          replace=False))))[:max(2, n_heads)]
+    fixed = [0, 1, 31, 32, 63, 64, block - 1, block, S // 2, S - 2, S - 1]
+    out = {}
+    for hd in heads:
+        rows = set(r for r in fixed if 0 <= r < S)
+        rows.update(rng.choice(S, size=min(n_rows, S), replace=False).tolist())
+        out[hd] = np.array(sorted(rows), dtype=np.int64)
+    return out
+
+
+def oracle_fwd_rows(bits, causal, scale, rows_by_head):
+    """Oracle O/LSE for the sampled rows: {head: (O [n,D], LSE [n])}."""
+    B, H, S, D = bits["q"].shape
+    q = bits["q"].reshape(B * H, S, D)
+    k = bits["k"].reshape(B * H, S, D)
+    v = bits["v"].reshape(B * H, S, D)
+    res = {}
+    for hd, rows in rows_by_head.items():
+        res[hd] = oracle.attn_fwd_rows(ai.bf16_bits_to_f64(q[hd, rows]), rows,
+                                       ai.bf16_bits_to_f64(k[hd]), ai.bf16_bits_to_f64(v[hd]),
+                                       scale, causal)
+    return res
+
+
+def fwd_errors(o, lse, o_ref, lse_ref):
+    do = np.abs(o - o_ref)
+    dl = np.abs(lse - lse_ref)
+    return {"o_max": float(do.max()), "o_mean": float(do.mean()), "lse_max": float(dl.max())}
+
+
+def assert_fwd_ok(err, what=""):
+    assert np.isfinite(err["o_max"]) and np.isfinite(err["lse_max"]), "%s non-finite %s" % (what,
+                                                                                             err)
+    assert err["o_max"] <= O_MAX, "%s O max err %.3e > %.1e (%s)" % (what, err["o_max"], O_MAX,
+                                                                     err)
+    assert err["o_mean"] <= O_MEAN, "%s O mean err %.3e > %.1e" % (what, err["o_mean"], O_MEAN)
+    assert err["lse_max"] <= LSE_MAX, "%s LSE err %.3e > %.1e" % (what, err["lse_max"], LSE_MAX)
+
+
+def sampled_fwd_errors(o, lse, bits, causal, scale, rows_by_head):
+    B, H, S, D = bits["q"].shape
+    ref = oracle_fwd_rows(bits, causal, scale, rows_by_head)
+    o = o.reshape(B * H, S, D)
+    lse = lse.reshape(B * H, S)
+    got_o, got_l, ref_o, ref_l = [], [], [], []
+    for hd, rows in rows_by_head.items():
+        got_o.append(o[hd, rows])
+        got_l.append(lse[hd, rows])
+        ref_o.append(ref[hd][0])
+        ref_l.append(ref[hd][1])
+    return fwd_errors(np.concatenate(got_o), np.concatenate(got_l), np.concatenate(ref_o),
+                      np.concatenate(ref_l))
+
+
+def bf16_ulp(x):
+    """Spacing of bf16 numbers at |x| (2^(e-7)); smallest normal spacing for 0."""
+    a = np.maximum(np.abs(x), 2.0 ** -126)
+    return 2.0 ** (np.floor(np.log2(a)) - 7)
+
+
+def gpu_fwd_bwd(bits, causal, scale):
+    """Forward then backward on cuda:0 (the backward consumes the GPU forward's O
+    and LSE).  Returns fp64 numpy (dQ, dK, dV)."""
+    import torch
+    import exact_attention_128_amd as A
+    dev = torch.device("cuda", 0)
+    q, k, v, do = (ai.to_torch_bf16(bits[n], dev) for n in ("q", "k", "v", "do"))
+    o, lse = A.fwd(q, k, v, causal=causal, scale=scale)
+    dq, dk, dv = A.bwd(q, k, v, o, lse, do, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return tuple(ai.bf16_bits_to_f64(ai.torch_bf16_to_bits(t)) for t in (dq, dk, dv))
+
+
+def oracle_bwd_heads(bits, causal, scale, heads):
+    """Oracle (dQ, dK, dV) for the listed heads of a [B,H,S,D] problem."""
+    B, H, S, D = bits["q"].shape
+    arr = {n: bits[n].reshape(B * H, S, D) for n in ("q", "k", "v", "do")}
+    out = {}
+    for hd in heads:
+        dq, dk, dv, _, _ = oracle.attn_bwd_head(*(ai.bf16_bits_to_f64(arr[n][hd])
+                                                  for n in ("q", "k", "v", "do")), scale, causal)
+        out[hd] = (dq, dk, dv)
+    return out
+
+
+def grad_errors(got, ref):
+    return {n: float(np.max(np.abs(g - r))) for n, g, r in zip(("dq", "dk", "dv"), got, ref)}
+
+
+def assert_grads_ok(err, what=""):
+    for n, e in err.items():
+        assert np.isfinite(e) and e <= GRAD_MAX, "%s %s max err %.3e > %.1e (%s)" % (
+            what, n, e, GRAD_MAX, err)

@@ -1,0 +1,72 @@
+"""GPU parity of the HIP backward (dQ, dK, dV) against the fp64 oracle.
+
+The backward consumes the GPU forward's O and LSE; the oracle recomputes its
+own fp64 forward.  Bound: max |err| <= 5e-2 for each gradient."""
+import numpy as np
+import pytest
+
+import attn_inputs as ai
+import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(B, H, S, D, causal, seed, scale=None):
+    bits = ai.make_inputs(B, H, S, D, seed, with_dout=True)
+    scale = 1.0 / np.sqrt(D) if scale is None else scale
+    got = P.gpu_fwd_bwd(bits, causal, scale)
+    ref = P.oracle_bwd_heads(bits, causal, scale, range(B * H))
+    ref = tuple(np.stack([ref[hd][i] for hd in range(B * H)]).reshape(B, H, S, D)
+                for i in range(3))
+    return P.grad_errors(got, ref), got
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("S", [1, 17, 64, 130, 300])
+def test_ragged_lengths(S, D, causal):
+    err, _ = _case(1, 2, S, D, causal, seed=2000 + S + D + int(causal))
+    P.assert_grads_ok(err, "S=%d D=%d causal=%s" % (S, D, causal))
+
+
+@pytest.mark.parametrize("scale", [1.0, -0.2, 0.0])
+def test_scale_values(scale):
+    """Off-standard scales.  The 5e-2 bound is stated for unit-variance inputs at
+    scale 1/sqrt(D); at scale 1 the gradients reach |dQ| ~ 40, where one bf16 ulp
+    of the output alone is 0.25.  So each gradient is held to
+    max(5e-2, 2^-7 * max|reference|): two bf16 ulps of its largest element."""
+    B, H, S, D = 1, 2, 150, 128
+    bits = ai.make_inputs(B, H, S, D, 31, with_dout=True)
+    got = P.gpu_fwd_bwd(bits, True, scale)
+    ref = P.oracle_bwd_heads(bits, True, scale, range(B * H))
+    for i, name in enumerate(("dq", "dk", "dv")):
+        r = np.stack([ref[hd][i] for hd in range(B * H)]).reshape(B, H, S, D)
+        bound = max(P.GRAD_MAX, 2.0 ** -7 * np.abs(r).max())
+        err = np.abs(got[i] - r).max()
+        assert np.isfinite(err) and err <= bound, "scale=%g %s err %.3e > %.3e" % (
+            scale, name, err, bound)
+
+
+def test_many_heads():
+    err, _ = _case(3, 50, 160, 128, True, seed=32)
+    P.assert_grads_ok(err, "many heads")
+
+
+def test_full_size_workload_sampled_heads():
+    """The causal backward workload (B=2, H=16, S=4096, D=128) in the benchmark's
+    launch configuration, compared in full on three heads, plus an invariant of
+    every head: sum_j dK_j = 0 (each row of dS sums to zero)."""
+    w = ai.WORKLOADS["bwd_causal_s4k"]
+    bits = ai.workload_inputs(w)
+    got = P.gpu_fwd_bwd(bits, w.causal, w.scale)
+    for g in got:
+        assert np.all(np.isfinite(g))
+    heads = [0, 13, w.B * w.H - 1]
+    ref = P.oracle_bwd_heads(bits, w.causal, w.scale, heads)
+    for hd in heads:
+        b, h = divmod(hd, w.H)
+        err = P.grad_errors([g[b, h] for g in got], ref[hd])
+        print("head", hd, err)
+        P.assert_grads_ok(err, "head %d" % hd)
+    colsum = np.abs(got[1].sum(axis=2)).max()
+    assert colsum <= 1.0, "sum_j dK_j far from zero: %.3e" % colsum

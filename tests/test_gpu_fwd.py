@@ -1,0 +1,101 @@
+"""GPU parity of the HIP forward against the fp64 oracle (through the C ABI)."""
+import numpy as np
+import pytest
+
+import attn_inputs as ai
+import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+def _full_case(B, H, S, D, causal, seed, scale=None, stress=False, rescale_log2=None):
+    bits = ai.make_inputs(B, H, S, D, seed, stress=stress)
+    scale = 1.0 / np.sqrt(D) if scale is None else scale
+    o, lse, _ = P.gpu_fwd(bits, causal, scale, rescale_log2)
+    o_ref, lse_ref = P.oracle_fwd_full(bits, causal, scale)
+    return P.fwd_errors(o, lse, o_ref, lse_ref)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_tiny_workload(causal):
+    w = ai.WORKLOADS["tiny"]
+    bits = ai.workload_inputs(w)
+    o, lse, _ = P.gpu_fwd(bits, causal, w.scale)
+    o_ref, lse_ref = P.oracle_fwd_full(bits, causal, w.scale)
+    P.assert_fwd_ok(P.fwd_errors(o, lse, o_ref, lse_ref), "tiny causal=%s" % causal)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("S", [1, 17, 64, 130, 1000])
+def test_ragged_lengths(S, D, causal):
+    err = _full_case(1, 3, S, D, causal, seed=1000 + S + D + int(causal))
+    P.assert_fwd_ok(err, "S=%d D=%d causal=%s" % (S, D, causal))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_many_heads(causal):
+    # 320 heads: the grid is several times the CU count, and B*H is not a
+    # multiple of 8 on one side (plain block order) and is on the other.
+    err = _full_case(2, 160, 200, 128, causal, seed=77)
+    P.assert_fwd_ok(err, "many heads")
+    err = _full_case(3, 5, 300, 64, causal, seed=78)
+    P.assert_fwd_ok(err, "odd heads")
+
+
+@pytest.mark.parametrize("scale", [1.0, -0.09, 0.0, 0.5])
+def test_scale_values(scale):
+    for causal in (False, True):
+        err = _full_case(1, 2, 190, 128, causal, seed=90, scale=scale)
+        P.assert_fwd_ok(err, "scale=%g causal=%s" % (scale, causal))
+
+
+def test_rescale_threshold_gives_same_result():
+    """Conditional rescaling is exact: every threshold matches the oracle.  Runs with
+    different thresholds use different stale maxima, so P is rounded to bf16 at
+    different points: each normalised weight carries a relative rounding error of at
+    most 2^-8 (P and l), hence two runs differ by at most 2 * 2^-8 * max|V| plus the
+    output rounding (1 ulp each)."""
+    bits = ai.make_inputs(1, 4, 3000, 128, 44, stress=True)
+    scale = 1.0 / np.sqrt(128)
+    o_ref, lse_ref = P.oracle_fwd_full(bits, True, scale)
+    vmax = np.abs(ai.bf16_bits_to_f64(bits["v"])).max(axis=(2, 3), keepdims=True)
+    outs = {}
+    for tau in (0.0, 8.0, 20.0):
+        o, lse, _ = P.gpu_fwd(bits, True, scale, rescale_log2=tau)
+        P.assert_fwd_ok(P.fwd_errors(o, lse, o_ref, lse_ref), "tau=%g" % tau)
+        outs[tau] = o
+    for tau in (8.0, 20.0):
+        diff = np.abs(outs[tau] - outs[0.0])
+        bound = 2 * 2.0 ** -8 * vmax + 2 * P.bf16_ulp(o_ref)
+        assert np.all(diff <= bound), "tau=%g vs 0: max diff %.3e" % (tau, diff.max())
+
+
+def test_deterministic():
+    bits = ai.make_inputs(2, 4, 777, 128, 5)
+    _, l1, b1 = P.gpu_fwd(bits, True, 0.1)
+    _, l2, b2 = P.gpu_fwd(bits, True, 0.1)
+    assert np.array_equal(b1, b2) and np.array_equal(l1, l2)
+
+
+def test_non_default_stream():
+    import torch
+    bits = ai.make_inputs(1, 8, 513, 128, 6)
+    s = torch.cuda.Stream()
+    o, lse, _ = P.gpu_fwd(bits, False, 1.0 / np.sqrt(128), stream=s)
+    o_ref, lse_ref = P.oracle_fwd_full(bits, False, 1.0 / np.sqrt(128))
+    P.assert_fwd_ok(P.fwd_errors(o, lse, o_ref, lse_ref), "side stream")
+
+
+@pytest.mark.parametrize("name", ["fwd_s2k", "fwd_causal_s8k", "fwd_stress_s16k"])
+def test_full_size_workloads_sampled(name):
+    """Full-size workloads in the benchmark's launch configuration, checked on
+    sampled rows (sequence and tile edges plus random rows of several heads)."""
+    w = ai.WORKLOADS[name]
+    bits = ai.workload_inputs(w)
+    o, lse, _ = P.gpu_fwd(bits, w.causal, w.scale)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    rows = P.sample_rows(w.B, w.H, w.S, n_heads=4, n_rows=96, seed=w.seed)
+    err = P.sampled_fwd_errors(o, lse, bits, w.causal, w.scale, rows)
+    print(name, err)
+    P.assert_fwd_ok(err, name)
