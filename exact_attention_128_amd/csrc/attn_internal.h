@@ -23,6 +23,7 @@ struct FwdParams {
   uint32_t qxor;  // applied to every Q word pair: 0 (scale > 0) or 0x80008000 (scale < 0)
   uint32_t qand;  // 0xffffffff, or 0 when scale == 0 (Q treated as zero)
   float tau;      // rescale threshold in log2 units
+  float thresh;   // 2^tau: a lane's partial weight sum above it triggers a rescale
   int xcd_heads;  // heads per XCD for the XCD-aware block order, 0 = plain order
 };
 

@@ -99,3 +99,26 @@ def test_full_size_workloads_sampled(name):
     err = P.sampled_fwd_errors(o, lse, bits, w.causal, w.scale, rows)
     print(name, err)
     P.assert_fwd_ok(err, name)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_large_score_jump(causal):
+    """A late key whose score exceeds every earlier score by ~150 nats (over 128
+    in log2 units), so the weights computed against the stale row maximum
+    overflow to inf and the rescale path must recover from the kept exponents.
+    Queries are 2u and key 600 is 7u for one random sign vector u (exact in
+    bf16); every other key is N(0,1)."""
+    B, H, S, D = 1, 2, 700, 128
+    bits = ai.make_inputs(B, H, S, D, 4242)
+    rng = np.random.default_rng(4243)
+    u = np.where(rng.random(D) < 0.5, -1.0, 1.0).astype(np.float32)
+    q = np.broadcast_to(2.0 * u, (B, H, S, D))
+    k = ai.bf16_bits_to_f32(bits["k"]).copy()
+    k[:, :, 600, :] = 7.0 * u
+    bits["q"] = ai.f32_to_bf16_bits(q)
+    bits["k"] = ai.f32_to_bf16_bits(k)
+    scale = 1.0 / np.sqrt(D)
+    o, lse, _ = P.gpu_fwd(bits, causal, scale)
+    o_ref, lse_ref = P.oracle_fwd_full(bits, causal, scale)
+    assert lse_ref.max() > 150.0
+    P.assert_fwd_ok(P.fwd_errors(o, lse, o_ref, lse_ref), "score jump causal=%s" % causal)
