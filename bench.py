@@ -2,8 +2,8 @@
 """Benchmark of the fused exact-attention hot path on one MI355X.
 
 One step = the whole path over one batch of seeded synthetic input: the fused
-forward (O, LSE) followed by the backward (Delta, dK/dV with dQ accumulation,
-dQ cast) that consumes the forward's O and LSE.  The default workload is the
+forward (O, LSE) followed by the backward (row statistics, dK/dV, dQ) that
+consumes the forward's O and LSE.  The default workload is the
 causal backward workload (B=2, H=16, S=4096, D=128, bf16), the one workload
 that exercises every step.  Throughput is algorithmic TFLOPS: forward
 4*B*H*S^2*D (halved when causal) plus backward 2.5x that.

@@ -83,7 +83,7 @@ def bwd_workspace_size(B: int, H: int, S: int, D: int) -> int:
     return int(_lib.load().attn_bwd_workspace_size(B, H, S, D))
 
 
-BWD_PRE, BWD_MAIN, BWD_CAST, BWD_ALL = 1, 2, 4, 7
+BWD_PRE, BWD_MAIN, BWD_DQ, BWD_ALL = 1, 2, 4, 7
 
 
 def bwd_out(q, k, v, o, lse, do, dq, dk, dv, workspace, causal: bool = False,

@@ -24,7 +24,6 @@ COMMON = [
     "-std=c++20", "-O3", "-fPIC", "--offload-arch=" + ARCH,
     # no packed-fp32 VALU forms: keep every fp32 op scalar per lane
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-munsafe-fp-atomics",          # hardware fp32 atomic add for the dQ accumulator
     "-I" + os.path.join(ROOT, "include"),
     "-Wall", "-Wno-unused-function",
 ]

@@ -20,6 +20,8 @@ int check_shape(int B, int H, int S, int D) {
   const int64_t bh = int64_t(B) * H;
   if (bh > 0x7fffffffLL) return ATTN_ERR_SHAPE;
   if (bh * S * D >= kMaxElems) return ATTN_ERR_SHAPE;
+  // the kernels address one head's [S][D] bf16 slab with 32-bit byte offsets
+  if (int64_t(S) * D >= (int64_t(1) << 29)) return ATTN_ERR_SHAPE;
   return ATTN_OK;
 }
 
@@ -81,8 +83,9 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
 
 size_t attn_bwd_workspace_size(int B, int H, int S, int D) {
   if (check_shape(B, H, S, D) != ATTN_OK) return 0;
-  const size_t rows = size_t(B) * H * S;
-  return round_up(rows * sizeof(float), 256) + round_up(rows * D * sizeof(float), 256);
+  (void)D;
+  const size_t stat_bytes = size_t(B) * H * ((S + 63) / 64) * 128 * sizeof(float);
+  return round_up(stat_bytes, 256);
 }
 
 int attn_bwd_phases(const void* q, const void* k, const void* v, const void* o,
@@ -100,7 +103,6 @@ int attn_bwd_phases(const void* q, const void* k, const void* v, const void* o,
   if (!isfinite(scale)) return ATTN_ERR_SCALE;
   if (workspace_bytes < attn_bwd_workspace_size(B, H, S, D)) return ATTN_ERR_WORKSPACE;
 
-  const size_t rows = size_t(B) * H * S;
   attn::BwdParams p{};
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint16_t*>(k);
@@ -111,11 +113,11 @@ int attn_bwd_phases(const void* q, const void* k, const void* v, const void* o,
   p.dq = static_cast<uint16_t*>(dq);
   p.dk = static_cast<uint16_t*>(dk);
   p.dv = static_cast<uint16_t*>(dv);
-  p.delta = static_cast<float*>(workspace);
-  p.dqacc = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                     round_up(rows * sizeof(float), 256));
+  p.nblk = (S + 63) / 64;
+  p.stats = static_cast<float*>(workspace);
   p.bh = B * H;
   p.S = S;
+  p.xcd_heads = (p.bh % 8 == 0) ? p.bh / 8 : 0;
   p.scale = scale;
   p.c = scale * attn::kLog2eHost;
   if (phases == 0 || (phases & ~unsigned(ATTN_BWD_ALL)) != 0) return ATTN_ERR_UNSUPPORTED;

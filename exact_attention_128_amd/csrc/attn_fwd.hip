@@ -61,8 +61,6 @@
 //
 // l is summed from the bf16-rounded P that the PV product consumes (so a row
 // dominated by one key normalises exactly), and separately in fp32 for the LSE.
-#include <utility>
-
 #include "attn_internal.h"
 #include "gfx950.h"
 
@@ -80,62 +78,6 @@ struct FwdTile {
   // one per (V feature block, 16-key group) (16 keys x 64 bytes).
   static constexpr int NPIECE = CH + DB * (BC / 16);
 };
-
-// Scheduling groups for a matrix half: NQ score products (one 16-byte LDS read
-// each) then NM - NQ output products (two 8-byte transposing reads each).
-// The reads of the first LA products go first; after product i come the reads
-// that product i + LA needs.
-template <int NQ, int NM, int LA>
-struct MSched {
-  static constexpr int need(int i) { return i < NQ ? i + 1 : NQ + 2 * (i - NQ + 1); }
-  template <int I>
-  static __device__ __forceinline__ void step() {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    constexpr int more = (I + LA < NM) ? need(I + LA) - need(I + LA - 1) : 0;
-    if constexpr (more > 0) __builtin_amdgcn_sched_group_barrier(0x100, more, 0);
-  }
-  template <int... I>
-  static __device__ __forceinline__ void all(std::integer_sequence<int, I...>) {
-    (step<I>(), ...);
-  }
-  static __device__ __forceinline__ void apply() {
-    __builtin_amdgcn_sched_group_barrier(0x100, need(LA - 1), 0);
-    all(std::make_integer_sequence<int, NM>{});
-  }
-};
-
-// One direct-to-LDS load: each lane's 16 bytes at buffer offset voff + soff
-// land at dst + 16 * lane.  Issued as inline assembly on purpose: the kernel
-// orders these loads against its LDS reads itself (a vmcnt wait plus a
-// barrier per tile), and a compiler that sees the LDS write adds conservative
-// waits for it in front of unrelated LDS reads.  The memory clobber keeps LDS
-// accesses from moving across it.
-// (Nothing else in these kernels uses m0, so clobbering it is safe.)
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void lds_dma16(ATTN_LDS char* dst, u32x4 rsrc, int voff, int soff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :
-               : "s"((uint32_t)(uintptr_t)dst), "v"(voff), "s"(rsrc), "s"(soff)
-               : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-// vmcnt(n) with the other counters left alone (gfx9 encoding)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
-}
-
-// Raw buffer descriptor (gfx9 layout) over nbytes at base, in SGPRs.
-__device__ __forceinline__ u32x4 buffer_rsrc(const void* base, uint32_t nbytes) {
-  const uint64_t a = (uint64_t)(uintptr_t)base;
-  const u32x4 r = {(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
-                   (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32)) & 0xffffu,
-                   (uint32_t)__builtin_amdgcn_readfirstlane((int)nbytes), 0x00020000u};
-  return r;
-}
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))

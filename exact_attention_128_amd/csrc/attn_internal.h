@@ -38,15 +38,19 @@ struct BwdParams {
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
-  float* delta;   // [B*H][S] fp32 workspace
-  float* dqacc;   // [B*H][S][D] fp32 workspace
+  float* stats;   // workspace [B*H][nblk][2][64] fp32: per 64-row block, LSE*log2(e)
+                  // of each row, then Delta of each row (zero for rows past S)
   int bh;
   int S;
+  int nblk;       // 64-row blocks per head, ceil(S / 64)
+  int nqb;        // query blocks per head of the dQ kernel
   float scale;    // the logit scale (any finite value)
   float c;        // scale * log2(e)
+  int xcd_heads;  // heads per XCD for the XCD-aware block order, 0 = plain order
 };
 
 hipError_t launch_fwd(const FwdParams& p, int D, bool causal, hipStream_t stream);
 hipError_t launch_bwd(const BwdParams& p, int D, bool causal, unsigned phases, hipStream_t stream);
+hipError_t launch_bwd_dq(const BwdParams& p, int D, bool causal, hipStream_t stream);
 
 }  // namespace attn

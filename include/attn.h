@@ -50,7 +50,7 @@ typedef struct ihipStream_t* attn_stream_t;
 enum attn_status {
   ATTN_OK = 0,
   ATTN_ERR_NULL = 1,        /* a required pointer is NULL                         */
-  ATTN_ERR_SHAPE = 2,       /* B, H or S < 1, or B*H*S*D >= 2^40                  */
+  ATTN_ERR_SHAPE = 2,       /* B, H or S < 1, B*H*S*D >= 2^40, or S*D >= 2^29     */
   ATTN_ERR_HEAD_DIM = 3,    /* D is not 64 or 128                                 */
   ATTN_ERR_ALIGN = 4,       /* a bf16 tensor not 16-byte aligned, LSE not 4-byte,
                                or the workspace not 256-byte aligned              */
@@ -94,8 +94,9 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
 
 /*
  * Bytes of device workspace attn_bwd needs for this shape (0 if the shape is
- * invalid): an fp32 row statistic Delta_i = sum_d dO_id * O_id [B][H][S] and an
- * fp32 dQ accumulator [B][H][S][D], each 256-byte aligned.
+ * invalid): two fp32 row statistics per query row, LSE_i * log2(e) and
+ * Delta_i = sum_d dO_id * O_id, stored per 64-row block ([B][H][ceil(S/64)]
+ * [2][64]), rounded up to 256 bytes.
  */
 size_t attn_bwd_workspace_size(int B, int H, int S, int D);
 
@@ -108,8 +109,9 @@ size_t attn_bwd_workspace_size(int B, int H, int S, int D);
  *   workspace    device memory of at least attn_bwd_workspace_size(B,H,S,D)
  *                bytes, 256-byte aligned, owned by the caller; its contents
  *                on entry do not matter and are garbage on return.
- * dQ is accumulated with fp32 atomics, so its low bits may differ between
- * runs; dK and dV are deterministic.  Enqueues three kernels on `stream`.
+ * Every output is deterministic (no atomics).  Enqueues three kernels on
+ * `stream`: the row statistics, dK/dV (one workgroup per 128-key block), and
+ * dQ (one workgroup per 256-row query block).
  */
 int attn_bwd(const void* q, const void* k, const void* v, const void* o,
              const float* lse, const void* dout, void* dq, void* dk, void* dv,
@@ -118,18 +120,18 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o,
 
 /* Phases of the backward, for attn_bwd_phases. */
 enum attn_bwd_phase {
-  ATTN_BWD_PRE = 1,   /* Delta = rowsum(dO * O) into the workspace; zero the dQ accumulator */
-  ATTN_BWD_MAIN = 2,  /* dK, dV written; dQ accumulated into the workspace                  */
-  ATTN_BWD_CAST = 4,  /* dQ = bf16(scale * accumulator)                                     */
+  ATTN_BWD_PRE = 1,   /* LSE*log2(e) and Delta = rowsum(dO * O) into the workspace */
+  ATTN_BWD_MAIN = 2,  /* dK, dV written (reads the workspace)                      */
+  ATTN_BWD_DQ = 4,    /* dQ written (reads the workspace)                          */
   ATTN_BWD_ALL = 7
 };
 
 /*
  * attn_bwd restricted to the phases set in `phases` (a nonzero subset of
- * ATTN_BWD_ALL), enqueued in the order PRE, MAIN, CAST.  A phase reads what the
- * earlier phases left in `workspace`, so running MAIN without a preceding PRE
- * on the same workspace adds onto the previous accumulator.  For callers that
- * time or schedule the phases separately; arguments otherwise as attn_bwd.
+ * ATTN_BWD_ALL), enqueued in the order PRE, MAIN, DQ.  MAIN and DQ read the
+ * statistics PRE left in `workspace` (for the same o, lse, dout), and are
+ * independent of each other.  For callers that time or schedule the phases
+ * separately; arguments otherwise as attn_bwd.
  * phases == 0 or outside ATTN_BWD_ALL: ATTN_ERR_UNSUPPORTED.
  */
 int attn_bwd_phases(const void* q, const void* k, const void* v, const void* o,
