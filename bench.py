@@ -9,8 +9,9 @@ that exercises every step.  Throughput is algorithmic TFLOPS: forward
 4*B*H*S^2*D (halved when causal) plus backward 2.5x that.
 
 Also measured, in the same process:
-  * the dominant kernel (the backward main kernel) on its own, timed with HIP
-    events on the stream it is launched on -> "roofline" (MFMA bound);
+  * the dominant kernel (the backward's dK/dV kernel) on its own, timed with
+    HIP events on the stream it is launched on -> "roofline" (MFMA bound); the
+    backward's dQ kernel likewise -> "dq_kernel";
   * the forward alone on the three forward workloads (S=2048 non-causal, S=8192
     causal, S=16384 causal rising-maximum) -> "legs" and "fwd_roofline";
   * the fp64 CPU oracle on a bounded sample of the same workload on this host's
@@ -113,17 +114,25 @@ def main():
         torch.cuda.synchronize()
         return a.elapsed_time(b) / n
 
-    # dominant kernel: backward main (run PRE once so the workspace holds Delta)
+    # The dominant kernel is the backward's dK/dV kernel (run PRE once so the
+    # workspace holds the row statistics).  Its algorithmic work is four of the
+    # backward's five products (S, dP, dV, dK): 0.8 of the backward FLOPs.  The
+    # dQ kernel's algorithmic work is the fifth (dQ); it also recomputes S and
+    # dP, which the count leaves out.
     A.bwd_out(q, k, v, o, lse, do, dq, dk, dv, ws, causal=causal, scale=scale, phases=A.BWD_PRE)
     n_rep = max(args.steps, 10)
     ms_main = time_launches(lambda: A.bwd_out(q, k, v, o, lse, do, dq, dk, dv, ws, causal=causal,
                                               scale=scale, phases=A.BWD_MAIN), n_rep)
+    ms_dq = time_launches(lambda: A.bwd_out(q, k, v, o, lse, do, dq, dk, dv, ws, causal=causal,
+                                            scale=scale, phases=A.BWD_DQ), n_rep)
     ms_fwd = time_launches(lambda: A.fwd_out(q, k, v, o, lse, causal=causal, scale=scale), n_rep)
     ms_bwd = time_launches(lambda: A.bwd_out(q, k, v, o, lse, do, dq, dk, dv, ws, causal=causal,
                                              scale=scale), n_rep)
-    main_tflops = f_bwd / (ms_main * 1e-3) / 1e12
-    log("bwd main %.3f ms (%.1f TFLOPS), fwd %.3f ms, bwd total %.3f ms" % (
-        ms_main, main_tflops, ms_fwd, ms_bwd))
+    main_tflops = 0.8 * f_bwd / (ms_main * 1e-3) / 1e12
+    dq_alg_tflops = 0.2 * f_bwd / (ms_dq * 1e-3) / 1e12
+    dq_exec_tflops = 0.6 * f_bwd / (ms_dq * 1e-3) / 1e12
+    log("bwd dK/dV %.3f ms (%.1f TFLOPS), dQ %.3f ms (%.1f executed TFLOPS), fwd %.3f ms, "
+        "bwd total %.3f ms" % (ms_main, main_tflops, ms_dq, dq_exec_tflops, ms_fwd, ms_bwd))
 
     legs = {}
     fwd_roof = None
@@ -196,7 +205,11 @@ def main():
         "roofline": {"kernel": "attn_bwd_main_kernel<128,causal>", "bound": "mfma",
                      "achieved": round(main_tflops, 1), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(main_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": None, "ms": round(ms_main, 4)},
+        "dq_kernel": {"kernel": "attn_bwd_dq_kernel<128,causal>", "ms": round(ms_dq, 4),
+                      "algorithmic_tflops": round(dq_alg_tflops, 1),
+                      "executed_tflops": round(dq_exec_tflops, 1),
+                      "executed_frac": round(dq_exec_tflops / PEAK_BF16_TFLOPS, 4)},
         "fwd_ms": round(ms_fwd, 4),
         "bwd_ms": round(ms_bwd, 4),
         "fwd_tflops": round(f_fwd / (ms_fwd * 1e-3) / 1e12, 1),

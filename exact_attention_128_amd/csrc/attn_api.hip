@@ -120,6 +120,9 @@ int attn_bwd_phases(const void* q, const void* k, const void* v, const void* o,
   p.xcd_heads = (p.bh % 8 == 0) ? p.bh / 8 : 0;
   p.scale = scale;
   p.c = scale * attn::kLog2eHost;
+  p.cq = scale == 0.0f ? 1.0f : fabsf(scale) * attn::kLog2eHost;
+  p.qxor = scale < 0.0f ? 0x80008000u : 0u;
+  p.qand = scale == 0.0f ? 0u : 0xffffffffu;
   if (phases == 0 || (phases & ~unsigned(ATTN_BWD_ALL)) != 0) return ATTN_ERR_UNSUPPORTED;
   return hip_status(
       attn::launch_bwd(p, D, causal != 0, phases, reinterpret_cast<hipStream_t>(stream)));

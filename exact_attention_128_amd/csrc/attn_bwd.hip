@@ -148,26 +148,26 @@ void attn_bwd_main_kernel(BwdParams p) {
   const int nsteps = (S - qfirst + BQ - 1) / BQ;
 
   // ---- step tiles HBM -> LDS stage: Q and dO as [chunk column][64 rows][16 B]
-  //      (one 1 KiB load per chunk column, lane l carrying row l; rows past S
-  //      read as zero), then the step's (L2, Delta) block.
+  //      (one 1 KiB load per chunk column, lane l carrying row l; rows past S,
+  //      and whole steps past the last, read as zero), then the step's
+  //      (L2, Delta) block, which every wave loads (identical bytes) so that
+  //      the issue has no wave-dependent branch.
+  static_assert(CH % NW == 0, "chunk columns must split evenly over the waves");
   const int row_off = lane * (2 * D);
-  auto fetch = [&](int step, int st) {
+  auto fetch = [&](int step, int st) __attribute__((always_inline)) {
     const int q0 = qfirst + step * BQ;
     ATTN_LDS char* base = lds + st * T::STAGE;
 #pragma unroll
-    for (int k = 0; k < PPW; ++k) {
-      const int i = w + NW * k;  // wave-uniform
-      if (i < CH)
-        lds_dma16(base + i * CSTR, qrs, row_off, q0 * (2 * D) + i * 16);
-      else if (i < 2 * CH)
-        lds_dma16(base + T::QT + (i - CH) * CSTR, ors, row_off, q0 * (2 * D) + (i - CH) * 16);
-      else if (i == 2 * CH)
-        lds_dma16(base + 2 * T::QT, srs, lane * 16, (q0 / BQ) * 512);
+    for (int k = 0; k < CH / NW; ++k) {
+      const int i = w + NW * k;
+      lds_dma16(base + i * CSTR, qrs, row_off, q0 * (2 * D) + i * 16);
+      lds_dma16(base + T::QT + i * CSTR, ors, row_off, q0 * (2 * D) + i * 16);
     }
+    lds_dma16(base + 2 * T::QT, srs, lane * 16, (q0 / BQ) * 512);
   };
 
-  // ---- the first step's tiles; K and V rows of this lane's key (B operands
-  //      of S and dP: features 16kk + 8h .. +7)
+  // ---- the first two steps' tiles; K and V rows of this lane's key (B
+  //      operands of S and dP: features 16kk + 8h .. +7)
   fetch(0, 0);
   bf16x8 kf[KK], vf[KK];
   {
@@ -186,6 +186,7 @@ void attn_bwd_main_kernel(BwdParams p) {
   }
   wait_all();
   barrier();
+  fetch(1, 1);
 
   f32x16 dv[DB], dk[DB];  // dV^T, dK^T: lane = key, registers = features
 #pragma unroll
@@ -205,85 +206,151 @@ void attn_bwd_main_kernel(BwdParams p) {
   const int qa_base = h * CSTR + l32 * 16;
   const int tra_base = (2 * (g & 1) + ((ts & 3) >> 1)) * CSTR + (4 * (g >> 1) + (ts >> 2)) * 16 +
                        8 * (ts & 1);
+  auto stage_ptr = [&](int st) { return (const ATTN_LDS char*)lds + st * T::STAGE; };
 
-  // One step: queries qfirst + 64i .. +63 in two 32-query blocks.
-  auto step = [&](int i, auto masked_t) __attribute__((always_inline)) {
+  // A operands of S and dP for 32-query block sb: Q then dO, per feature step
+  auto read_s = [&](const ATTN_LDS char* stage, int sb, bf16x8 (&f)[2 * KK]) {
+    const ATTN_LDS char* qa = stage + qa_base + 512 * sb;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      f[2 * kk] = lds_read_b128(qa + 2 * kk * CSTR);
+      f[2 * kk + 1] = lds_read_b128(qa + T::QT + 2 * kk * CSTR);
+    }
+  };
+  // (L2, Delta) of the block's queries 8g4 + 4h .. +3 (broadcast reads)
+  auto read_stats = [&](const ATTN_LDS char* stage, int sb, f32x4 (&lv)[4], f32x4 (&dl)[4]) {
+    const ATTN_LDS char* sp = stage + 2 * T::QT + 128 * sb + 16 * h;
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      lv[g4] = *(const ATTN_LDS f32x4*)(sp + 32 * g4);
+      dl[g4] = *(const ATTN_LDS f32x4*)(sp + 256 + 32 * g4);
+    }
+  };
+  // transposed A operands of dV^T (dO) and dK^T (Q): per (t, db) four reads
+  auto read_g = [&](const ATTN_LDS char* stage, int sb, i16x4 (&f)[8 * DB]) {
+    const ATTN_LDS char* ta = stage + tra_base + 512 * sb;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int o = 4 * db * CSTR + 256 * t, x = 4 * (DB * t + db);
+        f[x] = lds_read_tr16(ta + T::QT + o);
+        f[x + 1] = lds_read_tr16(ta + T::QT + o + 128);
+        f[x + 2] = lds_read_tr16(ta + o);
+        f[x + 3] = lds_read_tr16(ta + o + 128);
+      }
+  };
+  // S and dP: C[query][key], lane = key, register r = query 8(r/4) + 4h + r%4
+  auto mfma_s = [&](const bf16x8 (&f)[2 * KK], f32x16& s, f32x16& dp) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s[r] = 0.0f;
+      dp[r] = 0.0f;
+    }
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      s = mfma32(f[2 * kk], kf[kk], s);
+      dp = mfma32(f[2 * kk + 1], vf[kk], dp);
+    }
+  };
+  // P and dS of a 32-query block, packed to bf16 in query order
+  auto softmax = [&](auto masked_t, int qb0, const f32x16& s, const f32x16& dp,
+                     const f32x4 (&lv)[4], const f32x4 (&dl)[4], uint32_t (&pk)[8],
+                     uint32_t (&dsk)[8]) {
     constexpr bool MASKED = decltype(masked_t)::value;
-    const int st = i & 1;
-    const int q0 = qfirst + i * BQ;
-    if (i + 1 < nsteps) fetch(i + 1, st ^ 1);
-    const ATTN_LDS char* stage = lds + st * T::STAGE;
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      // S and dP: C[query][key], lane = key, register r = query 8(r/4) + 4h + r%4
-      f32x16 s, dp;
+    for (int g4 = 0; g4 < 4; ++g4) {
+      float pr[4], ds[4];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[r] = 0.0f;
-        dp[r] = 0.0f;
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * g4 + e;
+        float v = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lv[g4][e]));
+        bool vis = kvalid;
+        if constexpr (MASKED) vis = vis && key <= qb0 + 8 * g4 + 4 * h + e;
+        v = vis ? v : 0.0f;
+        pr[e] = v;
+        ds[e] = v * (dp[r] - dl[g4][e]);
       }
-      const ATTN_LDS char* qa = stage + qa_base + 512 * sb;
+      pk[2 * g4] = pack_bf16x2(pr[0], pr[1]);
+      pk[2 * g4 + 1] = pack_bf16x2(pr[2], pr[3]);
+      dsk[2 * g4] = pack_bf16x2(ds[0], ds[1]);
+      dsk[2 * g4 + 1] = pack_bf16x2(ds[2], ds[3]);
+    }
+  };
+  // dV^T += dO^T P, dK^T += Q^T dS
+  auto mfma_g = [&](const i16x4 (&f)[8 * DB], const uint32_t (&pk)[8], const uint32_t (&dsk)[8]) {
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        s = mfma32(lds_read_b128(qa + 2 * kk * CSTR), kf[kk], s);
-        dp = mfma32(lds_read_b128(qa + T::QT + 2 * kk * CSTR), vf[kk], dp);
-      }
-      // P and dS, packed to bf16 in query order (the B operands below)
-      uint32_t pk[8], dsk[8];
-      const ATTN_LDS char* sp = stage + 2 * T::QT + 128 * sb + 16 * h;
+    for (int t = 0; t < 2; ++t) {
+      const u32x4 pw = {pk[4 * t], pk[4 * t + 1], pk[4 * t + 2], pk[4 * t + 3]};
+      const u32x4 sw4 = {dsk[4 * t], dsk[4 * t + 1], dsk[4 * t + 2], dsk[4 * t + 3]};
+      const bf16x8 bp = __builtin_bit_cast(bf16x8, pw);
+      const bf16x8 bs = __builtin_bit_cast(bf16x8, sw4);
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const f32x4 lv = *(const ATTN_LDS f32x4*)(sp + 32 * g4);
-        const f32x4 dl = *(const ATTN_LDS f32x4*)(sp + 256 + 32 * g4);
-        float pr[4], ds[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * g4 + e;
-          float v = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lv[e]));
-          bool vis = kvalid;
-          if constexpr (MASKED) vis = vis && key <= q0 + 32 * sb + 8 * g4 + 4 * h + e;
-          v = vis ? v : 0.0f;
-          pr[e] = v;
-          ds[e] = v * (dp[r] - dl[e]);
-        }
-        pk[2 * g4] = pack_bf16x2(pr[0], pr[1]);
-        pk[2 * g4 + 1] = pack_bf16x2(pr[2], pr[3]);
-        dsk[2 * g4] = pack_bf16x2(ds[0], ds[1]);
-        dsk[2 * g4 + 1] = pack_bf16x2(ds[2], ds[3]);
-      }
-      // dV^T += dO^T P, dK^T += Q^T dS (A operands read transposed)
-      const ATTN_LDS char* ta = stage + tra_base + 512 * sb;
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const u32x4 pw = {pk[4 * t], pk[4 * t + 1], pk[4 * t + 2], pk[4 * t + 3]};
-        const u32x4 sw4 = {dsk[4 * t], dsk[4 * t + 1], dsk[4 * t + 2], dsk[4 * t + 3]};
-        const bf16x8 bp = __builtin_bit_cast(bf16x8, pw);
-        const bf16x8 bs = __builtin_bit_cast(bf16x8, sw4);
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const int o = 4 * db * CSTR + 256 * t;
-          dv[db] = mfma32(cat_tr(lds_read_tr16(ta + T::QT + o), lds_read_tr16(ta + T::QT + o + 128)),
-                          bp, dv[db]);
-          dk[db] = mfma32(cat_tr(lds_read_tr16(ta + o), lds_read_tr16(ta + o + 128)), bs, dk[db]);
-        }
+      for (int db = 0; db < DB; ++db) {
+        const int x = 4 * (DB * t + db);
+        dv[db] = mfma32(cat_tr(f[x], f[x + 1]), bp, dv[db]);
+        dk[db] = mfma32(cat_tr(f[x + 2], f[x + 3]), bs, dk[db]);
       }
     }
-    // this wave's loads of step i+1 have landed, then every wave's: stage st
-    // may be refilled and stage st^1 read
+  };
+
+  // One step: queries qfirst + 64i .. +63 as blocks A (first 32) and B, in
+  // four regions that keep the matrix core fed from one wave:
+  //   R1  S, dP of A                        reads: S/dP operands of B, stats of A
+  //   R2  S, dP of B      + P, dS of A      reads: transposed operands of A, stats of B
+  //   R3  dV, dK of A     + P, dS of B      reads: transposed operands of B
+  //   --  every LDS read of this stage done, step i+1's loads landed: barrier
+  //   R4  dV, dK of B     + loads of step i+2 into this stage, S/dP operands
+  //                         of step i+1's block A
+  // fa holds block A's S/dP operands on entry and the next step's on exit.
+  constexpr int NG = 8 * DB;
+  auto step = [&](int i, auto masked_t, bf16x8 (&fa)[2 * KK]) __attribute__((always_inline)) {
+    const int st = i & 1;
+    const int q0 = qfirst + i * BQ;
+    const ATTN_LDS char* stage = stage_ptr(st);
+    bf16x8 fb[2 * KK];
+    f32x4 lva[4], dla[4], lvb[4], dlb[4];
+    i16x4 ga[NG], gb[NG];
+    f32x16 sa, dpa, sb, dpb;
+    uint32_t pka[8], dsa[8], pkb[8], dsb[8];
+    // R1
+    read_s(stage, 1, fb);
+    read_stats(stage, 0, lva, dla);
+    mfma_s(fa, sa, dpa);
+    __builtin_amdgcn_sched_barrier(0);
+    // R2
+    read_g(stage, 0, ga);
+    read_stats(stage, 1, lvb, dlb);
+    mfma_s(fb, sb, dpb);
+    softmax(masked_t, q0, sa, dpa, lva, dla, pka, dsa);
+    __builtin_amdgcn_sched_barrier(0);
+    // R3
+    read_g(stage, 1, gb);
+    mfma_g(ga, pka, dsa);
+    softmax(masked_t, q0 + 32, sb, dpb, lvb, dlb, pkb, dsb);
+    __builtin_amdgcn_sched_barrier(0);
     wait_all();
     barrier();
+    // R4
+    fetch(i + 2, st);
+    read_s(stage_ptr(st ^ 1), 0, fa);
+    mfma_g(gb, pkb, dsb);
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   using Yes = std::integral_constant<bool, true>;
   using No = std::integral_constant<bool, false>;
+  bf16x8 fa[2 * KK];
+  read_s(stage_ptr(0), 0, fa);
   if constexpr (CAUSAL) {
     // keys k0 .. k0+127 against queries k0 .. k0+127: the only masked steps
-    step(0, Yes{});
-    if (nsteps > 1) step(1, Yes{});
-    for (int i = 2; i < nsteps; ++i) step(i, No{});
+    step(0, Yes{}, fa);
+    if (nsteps > 1) step(1, Yes{}, fa);
+    for (int i = 2; i < nsteps; ++i) step(i, No{}, fa);
   } else {
-    for (int i = 0; i < nsteps; ++i) step(i, No{});
+    for (int i = 0; i < nsteps; ++i) step(i, No{}, fa);
   }
+  wait_all();  // the loads of the (unused) steps past the end
 
   // dK = scale * dK^T, dV = dV^T, stored row-major as bf16
   if (kvalid) {

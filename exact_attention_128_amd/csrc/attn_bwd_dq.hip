@@ -99,8 +99,10 @@ void attn_bwd_dq_kernel(BwdParams p) {
   const int qrow = qw + l32;
   const size_t head = (size_t)bh * S * D;
 
-  // ---- this lane's query row: Q and dO as B operands (features 16kk + 8h ..
-  //      +7), -LSE*log2(e) and Delta (zero past S, which makes dS zero there)
+  // ---- this lane's query row: Q' (Q with the sign of the scale folded in,
+  //      so that the score multiplier cq is positive and a masked score of
+  //      -inf gives P = 0) and dO as B operands (features 16kk + 8h .. +7),
+  //      -LSE*log2(e) and Delta (zero past S, which makes dS zero there)
   bf16x8 qf[KK], df[KK];
   float nl2 = 0.0f, dlt = 0.0f;
   {
@@ -114,6 +116,8 @@ void attn_bwd_dq_kernel(BwdParams p) {
         a = *(const u32x4*)(Qr + 16 * kk);
         b = *(const u32x4*)(Or + 16 * kk);
       }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a[e] = (a[e] ^ p.qxor) & p.qand;
       qf[kk] = __builtin_bit_cast(bf16x8, a);
       df[kk] = __builtin_bit_cast(bf16x8, b);
     }
@@ -163,7 +167,7 @@ void attn_bwd_dq_kernel(BwdParams p) {
   for (int i = 0; i < DB; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[i][r] = 0.0f;
-  const float c = p.c;
+  const float c = p.cq;
 
   // Per-lane LDS offsets within a slot (each fragment adds a constant):
   //   16-byte reads: key 32b + l32, chunk column 2kk + h (K, then V)
@@ -248,13 +252,21 @@ void attn_bwd_dq_kernel(BwdParams p) {
     const int key0 = tile * BC;
     return (key0 + BC > S) || (CAUSAL && key0 + BC - 1 > qw);
   };
+  // Keys past S or above the diagonal get a score of -inf (so P = 0), on the
+  // tiles that have any; a separate pass keeps the common softmax branch-free.
+  // Element (b, r) holds key key0 + 4h + (32b + 8(r/4) + r%4).
+  auto mask = [&](int tile, f32x16 (&s)[2]) {
+    const int lim = (CAUSAL ? min(S - 1, qrow) : S - 1) - (tile * BC + 4 * h);
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (32 * b + 8 * (r >> 2) + (r & 3) > lim) s[b][r] = -INFINITY;
+  };
   // dS^T = P^T (dP^T - Delta), P^T = exp2(S^T c - LSE log2 e), packed to bf16
-  // in key order (the B operand of dQ^T); keys past S or above the diagonal
-  // get P = 0 on the tiles that have any.
-  auto softmax = [&](int tile, const f32x16 (&s)[2], const f32x16 (&dp)[2],
-                     uint32_t (&pk)[2][8]) {
-    const bool msk = needs_mask(tile);
-    const int key0 = tile * BC;
+  // in key order (the B operand of dQ^T).
+  auto softmax = [&](int tile, f32x16 (&s)[2], const f32x16 (&dp)[2], uint32_t (&pk)[2][8]) {
+    if (needs_mask(tile)) mask(tile, s);
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
@@ -263,11 +275,7 @@ void attn_bwd_dq_kernel(BwdParams p) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           const int r = 2 * i + e;
-          float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], c, nl2));
-          if (msk) {
-            const int key = key0 + 32 * b + 8 * (r >> 2) + 4 * h + (r & 3);
-            pv = (key < S && (!CAUSAL || key <= qrow)) ? pv : 0.0f;
-          }
+          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], c, nl2));
           d2[e] = pv * (dp[b][r] - dlt);
         }
         pk[b][i] = pack_bf16x2(d2[0], d2[1]);
@@ -279,28 +287,32 @@ void attn_bwd_dq_kernel(BwdParams p) {
   if (ntiles > 1) fetch(1, 1);
   if (ntiles > 2) fetch(2, 2);
   sync_data(0);
-  uint32_t pk[2][8];
+  uint32_t pk[2][8];     // dS^T of the tile whose dQ product comes next
+  f32x16 sx[2], dpx[2];  // scores of the tile whose softmax comes next
   if (wtiles > 0) {
-    f32x16 s[2], dp[2];
-    scores(0, s, dp);
-    softmax(0, s, dp, pk);
+    scores(0, sx, dpx);
+    softmax(0, sx, dpx, pk);
   }
 
-  // ---- main loop: the forward's schedule (tile j in slot j % 4; waves 4..7
-  //      one barrier behind waves 0..3; the matrix half at raised priority).
+  // ---- main loop: the forward's schedule.  Tile j lives in slot j % 4.
+  //      Each wave's step j is its matrix half (which first requests tile
+  //      j+3 into the slot tile j-1 used), a barrier, its softmax half, and a
+  //      barrier; waves 4..7 start one barrier late, so on every SIMD one
+  //      wave's matrix half (at raised priority) meets the other's softmax
+  //      half.  The barrier after which a wave next reads tile j+1 is the one
+  //      where it has waited for its own loads of that tile.
   const int grp = w >> 2;
   if (grp == 1) sync();
   for (int j = 0; j < ntiles; ++j) {
     if (j + 3 < ntiles) fetch(j + 3, (j + 3) & (NS - 1));
-    f32x16 sn[2], dpn[2];
     if (j < wtiles) {
       __builtin_amdgcn_s_setprio(1);
-      mphase((j + 1) & (NS - 1), j & (NS - 1), sn, dpn, pk);
+      mphase((j + 1) & (NS - 1), j & (NS - 1), sx, dpx, pk);
       __builtin_amdgcn_s_setprio(0);
     }
     if (grp == 0) sync();
     else sync_data(j + 1);
-    if (j + 1 < wtiles) softmax(j + 1, sn, dpn, pk);
+    if (j + 1 < wtiles) softmax(j + 1, sx, dpx, pk);
     if (grp == 0) sync_data(j + 1);
     else sync();
   }

@@ -46,6 +46,10 @@ struct BwdParams {
   int nqb;        // query blocks per head of the dQ kernel
   float scale;    // the logit scale (any finite value)
   float c;        // scale * log2(e)
+  float cq;       // |scale| * log2(e), or 1 when scale == 0 (always > 0); the dQ
+                  // kernel scores Q' K with Q' = Q with the sign of scale folded in:
+  uint32_t qxor;  //   applied to every Q word pair: 0, or 0x80008000 when scale < 0
+  uint32_t qand;  //   0xffffffff, or 0 when scale == 0 (Q' = 0)
   int xcd_heads;  // heads per XCD for the XCD-aware block order, 0 = plain order
 };
 
