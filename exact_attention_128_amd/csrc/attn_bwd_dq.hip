@@ -264,22 +264,29 @@ void attn_bwd_dq_kernel(BwdParams p) {
         if (32 * b + 8 * (r >> 2) + (r & 3) > lim) s[b][r] = -INFINITY;
   };
   // dS^T = P^T (dP^T - Delta), P^T = exp2(S^T c - LSE log2 e), packed to bf16
-  // in key order (the B operand of dQ^T).
-  auto softmax = [&](int tile, f32x16 (&s)[2], const f32x16 (&dp)[2], uint32_t (&pk)[2][8]) {
+  // in key order (the B operand of dQ^T).  The exponent arguments and dP - Delta
+  // come first, then all exponentials, then the products: a consumer right
+  // behind its v_exp_f32 would stall on the transcendental's latency.
+  auto softmax = [&](int tile, f32x16 (&s)[2], f32x16 (&dp)[2], uint32_t (&pk)[2][8]) {
     if (needs_mask(tile)) mask(tile, s);
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float d2[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int r = 2 * i + e;
-          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], c, nl2));
-          d2[e] = pv * (dp[b][r] - dlt);
-        }
-        pk[b][i] = pack_bf16x2(d2[0], d2[1]);
+      for (int r = 0; r < 16; ++r) {
+        s[b][r] = __builtin_fmaf(s[b][r], c, nl2);
+        dp[b][r] = dp[b][r] - dlt;
       }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[b][r] = __builtin_amdgcn_exp2f(s[b][r]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        pk[b][i] = pack_bf16x2(s[b][2 * i] * dp[b][2 * i], s[b][2 * i + 1] * dp[b][2 * i + 1]);
   };
 
   // ---- prologue: tiles 0, 1, 2 requested; tile 0's scores and dS.

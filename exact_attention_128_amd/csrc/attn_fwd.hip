@@ -68,15 +68,20 @@ namespace attn {
 
 template <int D>
 struct FwdTile {
-  static constexpr int BC = 64;             // keys per tile
-  static constexpr int CH = D / 8;          // 16-byte chunk columns of a K row
-  static constexpr int DB = D / 32;         // 32-feature blocks of a V row
-  static constexpr int KTILE = CH * BC * 16;
-  static constexpr int VTILE = DB * BC * 64;
-  static constexpr int SLOT = KTILE + VTILE;
-  // 1 KiB pieces per tile: one per K chunk column (64 keys x 16 bytes) and
-  // one per (V feature block, 16-key group) (16 keys x 64 bytes).
-  static constexpr int NPIECE = CH + DB * (BC / 16);
+  static constexpr int BC = 64;               // keys per sub-tile
+  static constexpr int CH = D / 8;            // 16-byte chunk columns of a K row
+  static constexpr int DB = D / 32;           // 32-feature blocks of a V row
+  static constexpr int KSUB = CH * BC * 16;   // K sub-tile [CH][64 keys][16 B]
+  static constexpr int VSUB = DB * BC * 64;   // V sub-tile [DB][64 keys][64 B]
+  static constexpr int KSLOT = 2 * KSUB;      // a step's 128 keys
+  static constexpr int VSLOT = 2 * VSUB;
+  static constexpr int NKS = 3;               // K ring slots
+  static constexpr int NVS = 2;               // V ring slots
+  static constexpr int LDS = NKS * KSLOT + NVS * VSLOT;
+  // 1 KiB pieces per step: K one per (sub-tile, chunk column), V one per
+  // (sub-tile, feature block, 16-key group); each group of 4 waves moves one.
+  static constexpr int KPIECE = 2 * CH;
+  static constexpr int VPIECE = 2 * DB * (BC / 16);
 };
 
 template <int D, bool CAUSAL>
@@ -86,20 +91,21 @@ void attn_fwd_kernel(FwdParams p) {
   constexpr int NW = 8;
   constexpr int BR = 32 * NW;
   constexpr int BC = T::BC;
-  constexpr int NS = 4;          // LDS ring slots
   constexpr int KK = D / 16;     // MFMA steps over the head dimension
   constexpr int DB = D / 32;     // 32-row blocks of O^T
   constexpr int CH = T::CH;
-  constexpr int NPW = T::NPIECE / NW;   // tile pieces per wave
-  static_assert(T::NPIECE % NW == 0, "tile pieces must split evenly over the waves");
+  constexpr int KPW = T::KPIECE / 4;   // K pieces per wave of waves 4..7
+  constexpr int VPW = T::VPIECE / 4;   // V pieces per wave of waves 0..3
+  static_assert(T::KPIECE % 4 == 0 && T::VPIECE % 4 == 0, "pieces must split over 4 waves");
 
-  __shared__ __attribute__((aligned(16))) char smem[NS * T::SLOT];  // [slot][K tile, V tile]
+  __shared__ __attribute__((aligned(16))) char smem[T::LDS];  // [K ring][V ring]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int l32 = lane & 31;
   const int h = lane >> 5;
+  const int grp = w >> 2;
   const int S = p.S;
 
   // ---- work unit: (head, query block).  Causal: heaviest query blocks first.
@@ -150,47 +156,48 @@ void attn_fwd_kernel(FwdParams p) {
     }
   }
 
-  // keys [0, kend) matter to this workgroup; this wave uses tiles [0, wtiles)
+  // keys [0, kend) matter to this workgroup, in steps of 2*BC; this wave uses
+  // steps [0, wsteps)
   const int kend = CAUSAL ? min(S, q0 + BR) : S;
-  const int ntiles = (kend + BC - 1) / BC;
+  const int nsteps = (kend + 2 * BC - 1) / (2 * BC);
   const int wend = CAUSAL ? min(S, qw + 32) : S;
-  const int wtiles = qw < S ? (wend + BC - 1) / BC : 0;
+  const int wsteps = qw < S ? (wend + 2 * BC - 1) / (2 * BC) : 0;
 
-  // ---- K/V tiles: HBM -> LDS slot directly (rows past S read as zero).
-  //      Wave w moves pieces w, w+8, ...: lane l of a K piece carries key l
-  //      of one chunk column, lane l of a V piece carries 16 bytes of key l/4
-  //      of one feature block, so every piece lands as one 1 KiB run.
+  // ---- K/V of a step: HBM -> LDS directly (rows past S read as zero).
+  //      Waves 4..7 move K, waves 0..3 move V.  Lane l of a K piece carries
+  //      key l of one chunk column; lane l of a V piece carries 16 bytes of key
+  //      l/4 of one feature block; every piece lands as one 1 KiB run.
   const u32x4 krs = buffer_rsrc(p.k + head, (uint32_t)S * D * 2);
   const u32x4 vrs = buffer_rsrc(p.v + head, (uint32_t)S * D * 2);
   const int kl_off = lane * (2 * D);
   const int vl_off = (lane >> 2) * (2 * D) + (lane & 3) * 16;
-  auto fetch = [&](int tile, int slot) {
-    const int key0 = tile * BC;
-    ATTN_LDS char* base = (ATTN_LDS char*)smem + slot * T::SLOT;
+  ATTN_LDS char* const kring = (ATTN_LDS char*)smem;
+  ATTN_LDS char* const vring = kring + T::NKS * T::KSLOT;
+  auto fetch_k = [&](int st) {   // waves 4..7
+    const int key0 = st * 2 * BC;
+    ATTN_LDS char* base = kring + (st % T::NKS) * T::KSLOT;
 #pragma unroll
-    for (int k = 0; k < NPW; ++k) {
-      const int i = w + NW * k;   // wave-uniform
-      if (i < CH) {
-        lds_dma16(base + i * 1024, krs, kl_off, key0 * (2 * D) + i * 16);
-      } else {
-        const int db = (i - CH) >> 2, rg = (i - CH) & 3;
-        lds_dma16(base + T::KTILE + db * (BC * 64) + rg * 1024, vrs, vl_off,
-                  (key0 + 16 * rg) * (2 * D) + db * 64);
-      }
+    for (int k = 0; k < KPW; ++k) {
+      const int i = (w - 4) + 4 * k;
+      const int u = i / CH, cc = i % CH;
+      lds_dma16(base + u * T::KSUB + cc * 1024, krs, kl_off, (key0 + u * BC) * (2 * D) + cc * 16);
     }
   };
-  // Barriers.  sync_data(k) first waits until this wave's loads of tile k+1
-  // have landed (the loads of tile k+2, if requested, may stay in flight), so
-  // after it every tile up to k+1 is in LDS for all waves.
+  auto fetch_v = [&](int st) {   // waves 0..3
+    const int key0 = st * 2 * BC;
+    ATTN_LDS char* base = vring + (st % T::NVS) * T::VSLOT;
+#pragma unroll
+    for (int k = 0; k < VPW; ++k) {
+      const int i = w + 4 * k;
+      const int u = i / (DB * 4), r = i % (DB * 4), db = r >> 2, rg = r & 3;
+      lds_dma16(base + u * T::VSUB + db * (BC * 64) + rg * 1024, vrs, vl_off,
+                (key0 + u * BC + 16 * rg) * (2 * D) + db * 64);
+    }
+  };
   auto sync = [&]() {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-  };
-  auto sync_data = [&](int k) {
-    if (k + 2 < ntiles) wait_vmcnt<NPW>();
-    else wait_vmcnt<0>();
-    sync();
   };
 
   f32x16 o[DB];
@@ -198,90 +205,80 @@ void attn_fwd_kernel(FwdParams p) {
   for (int i = 0; i < DB; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[i][r] = 0.0f;
-  float m_run = 0.0f;        // stale row max in log2 units (scores * c); set by tile 0
+  float m_run = 0.0f;        // stale row max in log2 units (scores * c); set by step 0
   float l_b = 0.0f;          // sum of bf16-rounded P (normalises O)
   float l_f = 0.0f;          // sum of fp32 P (for the LSE)
   const float c = p.c;
   const float thresh = p.thresh;   // 2^tau
 
-  // Per-lane LDS byte offsets within a slot; every fragment adds a constant.
+  // Per-lane LDS byte offsets within a sub-tile; every fragment adds a constant.
   //   K (A operand of S^T): key 32b + l32, chunk column 2kk + h.
-  //   V (transposing read, see lds_read_tr16): keys 32b + 16t + 8*half +
-  //   tr_key, features 32db + tr_d .. +3.
+  //   V (transposing read, see lds_read_tr16): keys 16t + 4*half + tr_key
+  //   (+8), features 32db + tr_d .. +3.
   const int kbase = h * (BC * 16) + l32 * 16;
-  const int vbase = T::KTILE + (4 * ((lane >> 4) >> 1) + ((lane & 15) >> 2)) * 64 +
+  const int vbase = (4 * ((lane >> 4) >> 1) + ((lane & 15) >> 2)) * 64 +
                     (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
-  auto slot_ptr = [&](int slot) { return (const ATTN_LDS char*)smem + slot * T::SLOT; };
+  auto kslot = [&](int st) { return (const ATTN_LDS char*)kring + (st % T::NKS) * T::KSLOT; };
+  auto vslot = [&](int st) { return (const ATTN_LDS char*)vring + (st % T::NVS) * T::VSLOT; };
 
-  // S^T of the tile in slot `slot`: two 32-key blocks
-  auto qk = [&](int slot, f32x16 (&s)[2]) {
-    const ATTN_LDS char* kb = slot_ptr(slot) + kbase;
+  // S^T of step st's 128 keys: s[2u + b] = sub-tile u, 32-key block b
+  auto qk = [&](int st, f32x16 (&s)[4]) {
+    const ATTN_LDS char* kb = kslot(st) + kbase;
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[b][r] = 0.0f;
+      for (int r = 0; r < 16; ++r) s[i][r] = 0.0f;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const bf16x8 a = lds_read_b128(kb + 2 * kk * (BC * 16) + 32 * b * 16);
-        s[b] = mfma32(a, qf[kk], s[b]);
-      }
-  };
-  // O^T += V^T P^T with the tile in slot `slot`
-  auto pv = [&](int slot, const uint32_t (&pk)[2][8]) {
-    const ATTN_LDS char* vb = slot_ptr(slot) + vbase;
+      for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const u32x4 pw = {pk[b][4 * t], pk[b][4 * t + 1], pk[b][4 * t + 2], pk[b][4 * t + 3]};
-        const bf16x8 bp = __builtin_bit_cast(bf16x8, pw);
-        const ATTN_LDS char* rb = vb + (32 * b + 16 * t) * 64;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const i16x4 x0 = lds_read_tr16(rb + db * (BC * 64));
-          const i16x4 x1 = lds_read_tr16(rb + db * (BC * 64) + 8 * 64);
-          const u32x4 aw = {__builtin_bit_cast(u32x2, x0)[0], __builtin_bit_cast(u32x2, x0)[1],
-                            __builtin_bit_cast(u32x2, x1)[0], __builtin_bit_cast(u32x2, x1)[1]};
-          o[db] = mfma32(__builtin_bit_cast(bf16x8, aw), bp, o[db]);
+        for (int b = 0; b < 2; ++b) {
+          const bf16x8 a = lds_read_b128(kb + u * T::KSUB + 2 * kk * (BC * 16) + 32 * b * 16);
+          s[2 * u + b] = mfma32(a, qf[kk], s[2 * u + b]);
         }
-      }
   };
-  // The matrix half: S^T of the tile in slot ks and O^T += V^T P^T with the
-  // tile in slot vs.  All fragment reads are written first and then
-  // interleaved with the products by scheduling groups, so each product finds
-  // its operands LA products ahead: LDS latency stays hidden without holding
-  // a whole tile in registers.
-  auto mphase = [&](int ks, int vs, f32x16 (&s)[2], const uint32_t (&pk)[2][8]) {
-    constexpr int NQ = 2 * KK, NP = 4 * DB, NM = NQ + NP, LA = 5;
-    const ATTN_LDS char* kb = slot_ptr(ks) + kbase;
-    const ATTN_LDS char* vb = slot_ptr(vs) + vbase;
+  // The matrix half: S^T of step ks and O^T += V^T P^T with the V of step
+  // vs.  All fragment reads are written first and then interleaved with the
+  // products by scheduling groups, so each product finds its operands LA
+  // products ahead: LDS latency stays hidden without holding a whole tile in
+  // registers.
+  auto mphase = [&](int ks, int vs, f32x16 (&s)[4], const uint32_t (&pk)[4][8]) {
+    constexpr int NQ = 4 * KK, NP = 8 * DB, NM = NQ + NP, LA = 5;
+    const ATTN_LDS char* kb = kslot(ks) + kbase;
+    const ATTN_LDS char* vb = vslot(vs) + vbase;
     bf16x8 kf[NQ];
     i16x4 vf[2 * NP];
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int b = 0; b < 2; ++b) kf[2 * kk + b] = lds_read_b128(kb + 2 * kk * (BC * 16) + 32 * b * 16);
+      for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
-    for (int bt = 0; bt < 4; ++bt)
+        for (int b = 0; b < 2; ++b)
+          kf[2 * KK * u + 2 * kk + b] =
+              lds_read_b128(kb + u * T::KSUB + 2 * kk * (BC * 16) + 32 * b * 16);
+#pragma unroll
+    for (int bt = 0; bt < 8; ++bt)
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const ATTN_LDS char* rb = vb + 16 * bt * 64 + db * (BC * 64);
+        const ATTN_LDS char* rb = vb + (bt >> 2) * T::VSUB + 16 * (bt & 3) * 64 + db * (BC * 64);
         vf[2 * (DB * bt + db)] = lds_read_tr16(rb);
         vf[2 * (DB * bt + db) + 1] = lds_read_tr16(rb + 8 * 64);
       }
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[b][r] = 0.0f;
+      for (int r = 0; r < 16; ++r) s[i][r] = 0.0f;
 #pragma unroll
-    for (int i = 0; i < NQ; ++i) s[i & 1] = mfma32(kf[i], qf[i >> 1], s[i & 1]);
+    for (int i = 0; i < NQ; ++i) {
+      const int u = i / (2 * KK), j = i % (2 * KK);
+      s[2 * u + (j & 1)] = mfma32(kf[i], qf[j >> 1], s[2 * u + (j & 1)]);
+    }
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
-      const int bt = i / DB, db = i % DB;
-      const u32x4 pw = {pk[bt >> 1][4 * (bt & 1)], pk[bt >> 1][4 * (bt & 1) + 1],
-                        pk[bt >> 1][4 * (bt & 1) + 2], pk[bt >> 1][4 * (bt & 1) + 3]};
+      const int bt = i / DB, db = i % DB;   // 16-key group bt of the step's 128 keys
+      const uint32_t* pp = &pk[bt >> 1][4 * (bt & 1)];
+      const u32x4 pw = {pp[0], pp[1], pp[2], pp[3]};
       const u32x2 a0 = __builtin_bit_cast(u32x2, vf[2 * i]);
       const u32x2 a1 = __builtin_bit_cast(u32x2, vf[2 * i + 1]);
       const u32x4 aw = {a0[0], a0[1], a1[0], a1[1]};
@@ -290,47 +287,45 @@ void attn_fwd_kernel(FwdParams p) {
     MSched<NQ, NM, LA>::apply();
   };
   // keys past the sequence end, and above the causal diagonal, get -inf
-  auto mask = [&](int tile, f32x16 (&s)[2]) {
-    const int key0 = tile * BC;
+  auto mask = [&](int st, f32x16 (&s)[4]) {
+    const int key0 = st * 2 * BC;
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = key0 + 32 * b + 8 * (r >> 2) + 4 * h + (r & 3);
+        const int key = key0 + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
         const bool vis = key < S && (!CAUSAL || key <= qrow);
-        if (!vis) s[b][r] = -INFINITY;
+        if (!vis) s[i][r] = -INFINITY;
       }
   };
-  auto needs_mask = [&](int tile) {
-    const int key0 = tile * BC;
-    return (key0 + BC > S) || (CAUSAL && key0 + BC - 1 > qw);
+  auto needs_mask = [&](int st) {
+    const int key0 = st * 2 * BC;
+    return (key0 + 2 * BC > S) || (CAUSAL && key0 + 2 * BC - 1 > qw);
   };
-  auto row_max = [&](const f32x16 (&s)[2]) {
+  auto row_max = [&](const f32x16 (&s)[4]) {
     float mx = s[0][0];
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[b][r]);
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[i][r]);
     return halfwave_max(mx);
   };
   // pack to bf16 (round to nearest even): the B operand of the PV product
-  auto pack = [&](const f32x16 (&e)[2], uint32_t (&pk)[2][8]) {
+  auto pack = [&](const f32x16 (&e)[4], uint32_t (&pk)[4][8]) {
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) pk[b][i] = pack_bf16x2(e[b][2 * i], e[b][2 * i + 1]);
+      for (int j = 0; j < 8; ++j) pk[i][j] = pack_bf16x2(e[i][2 * j], e[i][2 * j + 1]);
   };
-  // l_b += the rounded weights of a packed tile (exact products by 1, fp32 sum)
-  auto sum_packed = [&](const uint32_t (&pk)[2][8]) {
-    float a0 = l_b, a1 = 0.0f;
+  // l_b += the rounded weights of a packed step (exact products by 1, fp32
+  // sum; eight partial sums so that the adds do not wait on one another)
+  auto sum_packed = [&](const uint32_t (&pk)[4][8]) {
+    float a[8] = {l_b, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        if (i & 1) a1 = add_bf16x2(pk[b][i], a1);
-        else a0 = add_bf16x2(pk[b][i], a0);
-      }
-    l_b = a0 + a1;
+      for (int j = 0; j < 8; ++j) a[j] = add_bf16x2(pk[i][j], a[j]);
+    l_b = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
   };
   auto rescale = [&](float alpha) {
 #pragma unroll
@@ -340,33 +335,40 @@ void attn_fwd_kernel(FwdParams p) {
     l_b *= alpha;
     l_f *= alpha;
   };
-  // e = 2^(x - mx) for the kept exponents x; returns this lane's partial sum
-  auto expo = [&](const f32x16 (&x)[2], float mx, f32x16 (&e)[2]) {
-    float t0 = 0.0f, t1 = 0.0f;
+  // e = 2^(x - mx) for the kept exponents x; returns this lane's partial sum.
+  // All exponentials issue first and the sums follow behind a scheduling
+  // barrier: an add right behind its v_exp_f32 would stall on the
+  // transcendental's latency, which the compiler's schedule underestimates.
+  auto expo = [&](const f32x16 (&x)[4], float mx, f32x16 (&e)[4]) {
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        e[b][r] = __builtin_amdgcn_exp2f(x[b][r] - mx);
-        e[b][r + 1] = __builtin_amdgcn_exp2f(x[b][r + 1] - mx);
-        t0 += e[b][r];
-        t1 += e[b][r + 1];
-      }
-    return t0 + t1;
+      for (int r = 0; r < 16; ++r) e[i][r] = __builtin_amdgcn_exp2f(x[i][r] - mx);
+    __builtin_amdgcn_sched_barrier(0);
+    float t[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) t[k] = e[k >> 1][8 * (k & 1)];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if ((r & 7) != 0) t[2 * i + (r >> 3)] += e[i][r];
+    return ((t[0] + t[1]) + (t[2] + t[3])) + ((t[4] + t[5]) + (t[6] + t[7]));
   };
-  // Softmax of a later tile against the stale maximum m, with conditional
+  // Softmax of a later step against the stale maximum m, with conditional
   // rescaling.  x = s*c - m is kept until the weights e = 2^x have passed the
   // check, so the rare path needs no recomputation of the scores: it moves
   // each row's m up by its largest x (a row whose x never went positive keeps
   // m), scales O and the sums down to match, and redoes the exponentials.
   // Leaves the packed weights in pk and adds them into l_b.
-  auto softmax = [&](f32x16 (&s)[2], uint32_t (&pk)[2][8]) {
+  auto softmax = [&](f32x16 (&s)[4], uint32_t (&pk)[4][8]) {
     const float nm = -m_run;
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[b][r] = __builtin_fmaf(s[b][r], c, nm);
-    f32x16 e[2];
+      for (int r = 0; r < 16; ++r) s[i][r] = __builtin_fmaf(s[i][r], c, nm);
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16 e[4];
     float t = expo(s, 0.0f, e);
     if (wave_any(t > thresh)) {
       const float mx = fmaxf(row_max(s), 0.0f);
@@ -379,61 +381,79 @@ void attn_fwd_kernel(FwdParams p) {
     sum_packed(pk);
   };
 
-  // ---- prologue: tiles 0, 1, 2 requested; wait for 0 and 1; tile 0's
-  //      scores and softmax (the row maxima start exact).
-  fetch(0, 0);
-  if (ntiles > 1) fetch(1, 1);
-  if (ntiles > 2) fetch(2, 2);
-  sync_data(0);
+  // ---- prologue: K of steps 0..2 and V of step 0 requested; once K 0, K 1
+  //      and V 0 have landed, step 0's scores and softmax (the row maxima
+  //      start exact).
+  if (grp == 1) {
+    fetch_k(0);
+    if (nsteps > 1) fetch_k(1);
+    if (nsteps > 2) fetch_k(2);
+    if (nsteps > 2) wait_vmcnt<KPW>();
+    else wait_vmcnt<0>();
+  } else {
+    fetch_v(0);
+    wait_vmcnt<0>();
+  }
+  sync();
 
-  uint32_t pk[2][8];
-  if (wtiles > 0) {
-    f32x16 s[2], e[2];
+  uint32_t pk[4][8];
+  if (wsteps > 0) {
+    f32x16 s[4], e[4];
     qk(0, s);
     if (needs_mask(0)) mask(0, s);
     const float mx = row_max(s);
     m_run = mx == -INFINITY ? 0.0f : mx * c;   // every valid row sees key 0
     const float nm = -m_run;
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[b][r] = __builtin_fmaf(s[b][r], c, nm);
+      for (int r = 0; r < 16; ++r) s[i][r] = __builtin_fmaf(s[i][r], c, nm);
     l_f = expo(s, 0.0f, e);
     pack(e, pk);
     sum_packed(pk);
   }
 
-  // ---- main loop.  Tile j lives in slot j % 4.  Each wave's step j is its
-  //      matrix half (which first requests tile j+3 into the slot tile j-1
-  //      used), a barrier, its softmax half, and a barrier.  Waves 4..7 start
-  //      one barrier late, so their matrix half of step j runs beside the
-  //      softmax half of waves 0..3 and vice versa; the matrix half runs at
-  //      raised issue priority.  The barrier that ends half-step 2j+2 (after
-  //      the softmax half of waves 0..3, after the matrix half of waves 4..7)
-  //      is also where every wave waits for its loads of tile j+2, which
-  //      waves 0..3 first read right after it.  A wave at its last tile still
-  //      runs the score products of the (unused) next slot, so the matrix
-  //      half has a single code path.
-  const int g = w >> 2;
-  if (g == 1) sync();
-  for (int j = 0; j < ntiles; ++j) {
-    if (j + 3 < ntiles) fetch(j + 3, (j + 3) & (NS - 1));
-    f32x16 sn[2];
-    if (j < wtiles) {
+  // ---- main loop over steps of 128 keys.  K of step j lives in K slot j % 3,
+  //      V of step j in V slot j % 2.  Each wave's step j is its matrix half
+  //      (S^T of step j+1, O^T += V^T P^T of step j), a barrier, its softmax
+  //      half (step j+1), and a barrier; waves 4..7 start one barrier late,
+  //      so on every SIMD one wave's matrix half, at raised priority, meets
+  //      the other's softmax half.
+  //      Loads: waves 0..3 request V of step j+1 at the top of their step j
+  //      (into the slot step j-1 used, which every wave finished reading in
+  //      the barrier before) and wait for it at their second barrier, right
+  //      before anyone reads it.  Waves 4..7 request K of step j+3 at the top
+  //      of their step j (the slot of step j, whose scores every wave computed
+  //      a step earlier) and wait for K of step j+2 at their first barrier,
+  //      right before waves 0..3 read it.  A wave at its last step still runs
+  //      the score products of the (unused) next slot, so the matrix half has
+  //      a single code path.
+  if (grp == 1) sync();
+  for (int j = 0; j < nsteps; ++j) {
+    if (grp == 0) {
+      if (j + 1 < nsteps) fetch_v(j + 1);
+    } else {
+      if (j + 3 < nsteps) fetch_k(j + 3);
+    }
+    f32x16 sn[4];
+    if (j < wsteps) {
       __builtin_amdgcn_s_setprio(1);
-      mphase((j + 1) & (NS - 1), j & (NS - 1), sn, pk);
+      mphase(j + 1, j, sn, pk);
       __builtin_amdgcn_s_setprio(0);
     }
-    if (g == 0) sync();
-    else sync_data(j + 1);
-    if (j + 1 < wtiles) {
+    if (grp == 1) {
+      if (j + 3 < nsteps) wait_vmcnt<KPW>();
+      else wait_vmcnt<0>();
+    }
+    sync();
+    if (j + 1 < wsteps) {
       if (needs_mask(j + 1)) mask(j + 1, sn);
       softmax(sn, pk);
     }
-    if (g == 0) sync_data(j + 1);
-    else sync();
+    if (grp == 0) wait_vmcnt<0>();
+    sync();
   }
-  if (g == 0) sync();
+  if (grp == 0) sync();
 
   // ---- epilogue: O = O / l (bf16), LSE = ln2 * (m + log2 l)
   const float lb = halfwave_sum(l_b);
