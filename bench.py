@@ -34,6 +34,39 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
 PEAK_HBM_GBS = 8000.0
 
+# HBM bytes per launch of the dominant kernel (the backward's dK/dV kernel on
+# the causal S=4096 workload), from rocprofv3 FETCH_SIZE and WRITE_SIZE runs
+# (profiles/bwd_causal_s4k_counters.md), each scaled by what the same counter
+# reads for a plain 1 GiB device copy.  Valid only for the kernel sources whose
+# digest is recorded here; reported as null once they change.
+TRAFFIC_SOURCES = ("exact_attention_128_amd/csrc/attn_bwd.hip",
+                   "exact_attention_128_amd/csrc/gfx950.h",
+                   "exact_attention_128_amd/csrc/attn_internal.h")
+TRAFFIC = {"workload": "bwd_causal_s4k", "read_bytes": 222961083, "write_bytes": 67144907,
+           "sources_sha256": "be60bf2f437b642d7b2c58bdb0ead01d27f73ba991bf35ac0b4b1ed8107cd7d0"}
+# the same for the forward on the causal S=8192 workload
+# (profiles/fwd_causal_s8k_counters.md)
+FWD_TRAFFIC_SOURCES = ("exact_attention_128_amd/csrc/attn_fwd.hip",
+                       "exact_attention_128_amd/csrc/gfx950.h",
+                       "exact_attention_128_amd/csrc/attn_internal.h")
+FWD_TRAFFIC = {"workload": "fwd_causal_s8k", "read_bytes": 1359603838, "write_bytes": 136319061,
+               "sources_sha256": "f3a19ac47b68a4722587a23092eac2acd6233251ca3a01ccd1cf086e1d08ae17"}
+
+
+def measured_traffic(workload, record=None, sources=None):
+    import hashlib
+    record = TRAFFIC if record is None else record
+    sources = TRAFFIC_SOURCES if sources is None else sources
+    if workload != record["workload"]:
+        return None
+    h = hashlib.sha256()
+    for f in sources:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest() != record["sources_sha256"]:
+        return None
+    return record["read_bytes"] + record["write_bytes"]
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -54,7 +87,14 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time for the oracle sample")
+    ap.add_argument("--only", default=None,
+                    help="profiling driver: run one workload's kernels --steps times after "
+                         "--warmup runs and exit (a workload name, or 'copy' for a plain "
+                         "1 GiB device copy that calibrates the HBM byte counters)")
     args = ap.parse_args()
+    if args.only is not None:
+        run_only(args)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library's path has no multi-GPU "
@@ -161,7 +201,8 @@ def main():
         c3 = legs["fwd_causal_s8k"]
         fwd_roof = {"kernel": "attn_fwd_kernel<128,causal>", "workload": "fwd_causal_s8k",
                     "bound": "mfma", "achieved": c3["tflops"], "peak": PEAK_BF16_TFLOPS,
-                    "unit": "TFLOP/s", "frac": c3["frac_peak"], "traffic": None}
+                    "unit": "TFLOP/s", "frac": c3["frac_peak"],
+                    "traffic": measured_traffic("fwd_causal_s8k", FWD_TRAFFIC, FWD_TRAFFIC_SOURCES)}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -205,7 +246,7 @@ def main():
         "roofline": {"kernel": "attn_bwd_main_kernel<128,causal>", "bound": "mfma",
                      "achieved": round(main_tflops, 1), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(main_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "ms": round(ms_main, 4)},
+                     "traffic": measured_traffic(w.name), "ms": round(ms_main, 4)},
         "dq_kernel": {"kernel": "attn_bwd_dq_kernel<128,causal>", "ms": round(ms_dq, 4),
                       "algorithmic_tflops": round(dq_alg_tflops, 1),
                       "executed_tflops": round(dq_exec_tflops, 1),
@@ -219,6 +260,46 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def run_only(args):
+    """Run a single workload (or the calibration copy) for a profiler; prints
+    one line naming what ran."""
+    import torch
+    import attn_inputs as ai
+    import exact_attention_128_amd as A
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    if args.only == "copy":
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup + args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print("ran copy: %d launches of a %d-byte device copy" % (args.warmup + args.steps, n),
+              flush=True)
+        return
+    w = ai.WORKLOADS[args.only]
+    bits = ai.make_inputs(w.B, w.H, w.S, w.D, w.seed, stress=w.stress, with_dout=w.backward)
+    q, k, v = (ai.to_torch_bf16(bits[n], dev) for n in ("q", "k", "v"))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=dev)
+    if not w.backward:
+        for _ in range(args.warmup + args.steps):
+            A.fwd_out(q, k, v, o, lse, causal=w.causal, scale=w.scale)
+    else:
+        do = ai.to_torch_bf16(bits["do"], dev)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+        ws = torch.empty(A.bwd_workspace_size(w.B, w.H, w.S, w.D), dtype=torch.uint8, device=dev)
+        A.fwd_out(q, k, v, o, lse, causal=w.causal, scale=w.scale)
+        for _ in range(args.warmup + args.steps):
+            A.bwd_out(q, k, v, o, lse, do, dq, dk, dv, ws, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    print("ran %s: %d launches (%s)" % (w.name, args.warmup + args.steps,
+                                       "backward after one forward" if w.backward else "forward"),
+          flush=True)
 
 
 if __name__ == "__main__":
