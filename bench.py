@@ -12,8 +12,9 @@ Also measured, in the same process:
   * the dominant kernel (the backward's dK/dV kernel) on its own, timed with
     HIP events on the stream it is launched on -> "roofline" (MFMA bound); the
     backward's dQ kernel likewise -> "dq_kernel";
-  * the forward alone on the three forward workloads (S=2048 non-causal, S=8192
-    causal, S=16384 causal rising-maximum) -> "legs" and "fwd_roofline";
+  * the forward alone on the four forward workloads (S=128 D=64 non-causal, a
+    latency/HBM case reported with its algorithmic HBM rate; S=2048 non-causal;
+    S=8192 causal; S=16384 causal rising-maximum) -> "legs" and "fwd_roofline";
   * the fp64 CPU oracle on a bounded sample of the same workload on this host's
     cores -> "cpu_baseline" (a reported baseline, not the target).
 
@@ -179,7 +180,7 @@ def main():
     if not args.no_legs:
         del q, k, v, do, o, lse, dq, dk, dv, ws
         torch.cuda.empty_cache()
-        for name in ("fwd_s2k", "fwd_causal_s8k", "fwd_stress_s16k"):
+        for name in ("tiny", "fwd_s2k", "fwd_causal_s8k", "fwd_stress_s16k"):
             lw = ai.WORKLOADS[name]
             lb = ai.workload_inputs(lw)
             lq, lk, lv = (ai.to_torch_bf16(lb[n], dev) for n in ("q", "k", "v"))
@@ -191,11 +192,15 @@ def main():
                                                  scale=lw.scale), n_rep)
             fl = fwd_flops(lw.B, lw.H, lw.S, lw.D, lw.causal)
             tf = fl / (ms * 1e-3) / 1e12
+            # algorithmic HBM bytes: Q, K, V read and O written (bf16), LSE (fp32)
+            nbytes = 8.0 * lw.B * lw.H * lw.S * lw.D + 4.0 * lw.B * lw.H * lw.S
+            gbs = nbytes / (ms * 1e-3) / 1e9
             legs[name] = {"shape": [lw.B, lw.H, lw.S, lw.D], "causal": lw.causal,
-                          "ms": round(ms, 4), "tflops": round(tf, 1),
-                          "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
-            log("fwd leg %s: %.3f ms  %.1f TFLOPS (%.1f%%)" % (name, ms, tf,
-                                                               100 * tf / PEAK_BF16_TFLOPS))
+                          "ms": round(ms, 4), "tflops": round(tf, 2),
+                          "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                          "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+            log("fwd leg %s: %.4f ms  %.1f TFLOPS (%.1f%%)  %.1f GB/s algorithmic HBM" % (
+                name, ms, tf, 100 * tf / PEAK_BF16_TFLOPS, gbs))
             del lq, lk, lv, lo, ll
             torch.cuda.empty_cache()
         c3 = legs["fwd_causal_s8k"]
