@@ -42,7 +42,8 @@ PEAK_HBM_GBS = 8000.0
 # digest is recorded here; reported as null once they change.
 TRAFFIC_SOURCES = ("exact_attention_128_amd/csrc/attn_bwd.hip",
                    "exact_attention_128_amd/csrc/gfx950.h",
-                   "exact_attention_128_amd/csrc/attn_internal.h")
+                   "exact_attention_128_amd/csrc/attn_internal.h",
+                   "exact_attention_128_amd/build.py")
 TRAFFIC = {"workload": "bwd_causal_s4k", "read_bytes": 222961083, "write_bytes": 67144907,
            "sources_sha256": "be60bf2f437b642d7b2c58bdb0ead01d27f73ba991bf35ac0b4b1ed8107cd7d0"}
 # the same for the forward on the causal S=8192 workload

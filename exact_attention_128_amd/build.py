@@ -29,13 +29,23 @@ COMMON = [
 ]
 
 
+# Per-source flags.  attn_bwd.hip: one wave per SIMD may use 512 registers,
+# and with that budget the compiler would give every matrix product an AGPR
+# accumulator, so the softmax would copy each score back to a VGPR first;
+# the VGPR form keeps the scores in VGPRs (the dK/dV accumulators still spill
+# to AGPRs where needed).
+PER_SOURCE = {
+    "attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
 def _compile(src: str, outdir: str, extra) -> str:
     obj = os.path.join(outdir, os.path.basename(src) + ".o")
-    cmd = [HIPCC] + COMMON + list(extra) + ["-c", src, "-o", obj]
+    cmd = [HIPCC] + COMMON + PER_SOURCE.get(os.path.basename(src), []) + list(extra) + ["-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     msg = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
                     if "packed-fp32-ops' is not a recognized feature" not in l)

@@ -10,13 +10,14 @@
 // Two kernels here, on the caller's stream (dQ is computed by the kernel of
 // attn_bwd_dq.hip, which owns query rows and needs no atomics):
 //   pre    per 64-row block of each head: L2_i = LSE_i * log2(e) and
-//          Delta_i = sum_d dO_id * O_id (fp32, from the bf16 O), zero for the
-//          padding rows past S
+//          -Delta_i = -sum_d dO_id * O_id (fp32, from the bf16 O), zero for
+//          the padding rows past S
 //   main   dK, dV: one workgroup per (head, 128-key block); each of its 4 waves
 //          owns 32 keys, with their K and V rows resident in registers, and
 //          walks the query blocks that can see them, 64 queries per step:
 //            S   = Q K^T,  dP = dO V^T     (keys on lanes, queries in registers)
 //            P   = exp2(S * scale*log2e - L2),  dS = P (dP - Delta)
+//          (the dP accumulator starts at -Delta, so dS is a single product)
 //            dV^T += dO^T P,  dK^T += Q^T dS   (P, dS straight from registers)
 //
 // Memory pipeline.  Q, dO and the (L2, Delta) block of step i+1 travel from
@@ -62,10 +63,11 @@ struct BwdTile {
   static constexpr int KK = D / 16;          // MFMA steps over the features
   static constexpr int CSTR = BQ * 16 + 64;  // chunk column stride of a Q/dO tile
   static constexpr int QT = CH * CSTR;       // one Q or dO tile
-  static constexpr int STAT = 1024;          // [L2 x 64][Delta x 64] + landing room
+  static constexpr int STAT = 1024;          // [L2 x 64][-Delta x 64] + landing room
   static constexpr int STAGE = 2 * QT + STAT;
-  static constexpr int LDS = 2 * STAGE;
-  static constexpr int NPIECE = 2 * CH + 1;  // 1 KiB direct-to-LDS loads per step
+  static constexpr int LDS = 3 * STAGE;      // three stages in flight
+  static constexpr int NP = D / 8;           // matrix products per phase of a step
+  static constexpr int LA = 6;               // operand reads run this many products ahead
 };
 
 // ---------------------------------------------------------------- pre
@@ -95,18 +97,59 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(BwdParams p, long row
   if (rp < rows_pad && c == 0) {
     float* st = p.stats + bh * (long)per * 2 + (r / 64) * 128 + (r % 64);
     st[0] = valid ? p.lse[row] * kLog2e : 0.0f;
-    st[64] = valid ? acc : 0.0f;
+    st[64] = valid ? -acc : 0.0f;
   }
 }
 
 // ---------------------------------------------------------------- main
+//
+// One step = queries q0 .. q0+63 of one stage, as blocks A (first 32) and B.
+// Its 4*NP matrix products (NP = D/8) form one stream, in four phases:
+//   phase 0  S, dP of A      (operand: Q or dO rows, 16-byte reads)
+//   phase 1  S, dP of B
+//   phase 2  dV^T, dK^T of A (operand: dO^T or Q^T, two transposing reads)
+//   phase 3  dV^T, dK^T of B
+// The stream is issued in slots, one product per slot, in a fixed order
+// (scheduling barriers between slots): each product's LDS operand is read LA
+// products ahead of it, so no phase starts by draining the LDS queue, and the
+// softmax arithmetic of a block is cut into pairs of elements whose halves
+// (exponentials; products and bf16 packing) sit in slots of their own, so the
+// exponentials' latency passes while a product issues.  Three LDS stages:
+// the loads of step i+2 go to the stage step i-1 read, so the single barrier
+// of a step (before the reads of step i+1 start) waits only for loads issued
+// a step earlier and for no LDS read.
+template <int NP>
+struct BwdSlots {
+  static constexpr bool SPLIT = NP >= 16;  // pair halves in separate slots
+  static constexpr int first(int b) { return SPLIT ? (b + 1) * NP + 1 + b : (b + 1) * NP + 1; }
+  // slot after whose product half `part` (0: exponentials, 1: products and
+  // packing) of element pair k (0..7) of block b is issued
+  static constexpr int slot(int b, int k, int part) {
+    return SPLIT ? first(b) + 2 * k + part : first(b) + k;
+  }
+  // the first product that reads pair k of block b (query half k / 4)
+  static constexpr int need(int b, int k) { return (2 + b) * NP + (k < 4 ? 0 : NP / 2); }
+  static constexpr bool valid() {
+    for (int b = 0; b < 2; ++b)
+      for (int k = 0; k < 8; ++k)
+        if (slot(b, k, 1) >= need(b, k) || slot(b, k, 0) < (b + 1) * NP) return false;
+    return true;
+  }
+};
+
+template <int... M, class F>
+__device__ __forceinline__ void static_for(std::integer_sequence<int, M...>, F&& f) {
+  (f(std::integral_constant<int, M>{}), ...);
+}
+
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_bwd_main_kernel(BwdParams p) {
   using T = BwdTile<D>;
   constexpr int NW = 4, BQ = T::BQ, BK = T::BK, CH = T::CH, DB = T::DB, KK = T::KK;
-  constexpr int CSTR = T::CSTR;
-  constexpr int PPW = (T::NPIECE + NW - 1) / NW;
+  constexpr int CSTR = T::CSTR, QT = T::QT;
+  constexpr int NP = T::NP, LA = T::LA, NM = 4 * NP, NX = NM - LA;
+  static_assert(2 * KK == NP && 4 * DB == NP, "phase sizes");
 
   __shared__ __attribute__((aligned(16))) char smem[T::LDS];
   ATTN_LDS char* const lds = (ATTN_LDS char*)smem;
@@ -150,25 +193,25 @@ void attn_bwd_main_kernel(BwdParams p) {
   // ---- step tiles HBM -> LDS stage: Q and dO as [chunk column][64 rows][16 B]
   //      (one 1 KiB load per chunk column, lane l carrying row l; rows past S,
   //      and whole steps past the last, read as zero), then the step's
-  //      (L2, Delta) block, which every wave loads (identical bytes) so that
+  //      (L2, -Delta) block, which every wave loads (identical bytes) so that
   //      the issue has no wave-dependent branch.
   static_assert(CH % NW == 0, "chunk columns must split evenly over the waves");
   const int row_off = lane * (2 * D);
-  auto fetch = [&](int step, int st) __attribute__((always_inline)) {
+  auto fetch = [&](int step, ATTN_LDS char* base) __attribute__((always_inline)) {
     const int q0 = qfirst + step * BQ;
-    ATTN_LDS char* base = lds + st * T::STAGE;
 #pragma unroll
     for (int k = 0; k < CH / NW; ++k) {
       const int i = w + NW * k;
       lds_dma16(base + i * CSTR, qrs, row_off, q0 * (2 * D) + i * 16);
-      lds_dma16(base + T::QT + i * CSTR, ors, row_off, q0 * (2 * D) + i * 16);
+      lds_dma16(base + QT + i * CSTR, ors, row_off, q0 * (2 * D) + i * 16);
     }
-    lds_dma16(base + 2 * T::QT, srs, lane * 16, (q0 / BQ) * 512);
+    lds_dma16(base + 2 * QT, srs, lane * 16, (q0 / BQ) * 512);
   };
 
   // ---- the first two steps' tiles; K and V rows of this lane's key (B
   //      operands of S and dP: features 16kk + 8h .. +7)
-  fetch(0, 0);
+  fetch(0, lds);
+  fetch(1, lds + T::STAGE);
   bf16x8 kf[KK], vf[KK];
   {
     const uint16_t* Kr = p.k + head + (size_t)key * D + 8 * h;
@@ -186,7 +229,6 @@ void attn_bwd_main_kernel(BwdParams p) {
   }
   wait_all();
   barrier();
-  fetch(1, 1);
 
   f32x16 dv[DB], dk[DB];  // dV^T, dK^T: lane = key, registers = features
 #pragma unroll
@@ -206,149 +248,162 @@ void attn_bwd_main_kernel(BwdParams p) {
   const int qa_base = h * CSTR + l32 * 16;
   const int tra_base = (2 * (g & 1) + ((ts & 3) >> 1)) * CSTR + (4 * (g >> 1) + (ts >> 2)) * 16 +
                        8 * (ts & 1);
-  auto stage_ptr = [&](int st) { return (const ATTN_LDS char*)lds + st * T::STAGE; };
 
-  // A operands of S and dP for 32-query block sb: Q then dO, per feature step
-  auto read_s = [&](const ATTN_LDS char* stage, int sb, bf16x8 (&f)[2 * KK]) {
-    const ATTN_LDS char* qa = stage + qa_base + 512 * sb;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      f[2 * kk] = lds_read_b128(qa + 2 * kk * CSTR);
-      f[2 * kk + 1] = lds_read_b128(qa + T::QT + 2 * kk * CSTR);
+  // LDS operand of product m of a step (phases as above)
+  auto operand = [&](const ATTN_LDS char* stg, auto m_t) __attribute__((always_inline)) {
+    constexpr int m = decltype(m_t)::value, ph = m / NP, j = m % NP;
+    if constexpr (ph < 2) {
+      // S (j even: Q) or dP (j odd: dO), features 16(j/2) + 8h .. +7
+      return lds_read_b128(stg + qa_base + 512 * ph + (j & 1) * QT + (j >> 1) * 2 * CSTR);
+    } else {
+      // dV^T (j even: dO^T) or dK^T (j odd: Q^T) of feature block db, query
+      // half t of the block
+      constexpr int t = j / (2 * DB), db = (j / 2) % DB;
+      const ATTN_LDS char* b =
+          stg + tra_base + 512 * (ph - 2) + 4 * db * CSTR + 256 * t + ((j & 1) ? 0 : QT);
+      return cat_tr(lds_read_tr16(b), lds_read_tr16(b + 128));
     }
   };
-  // (L2, Delta) of the block's queries 8g4 + 4h .. +3 (broadcast reads)
-  auto read_stats = [&](const ATTN_LDS char* stage, int sb, f32x4 (&lv)[4], f32x4 (&dl)[4]) {
-    const ATTN_LDS char* sp = stage + 2 * T::QT + 128 * sb + 16 * h;
+  // L2 of the block's queries 8g4 + 4h .. +3 (broadcast reads), and their
+  // -Delta as the starting value of the dP accumulator (same register order)
+  auto read_stats = [&](const ATTN_LDS char* stg, int sb, f32x4 (&lv)[4], f32x16& dp) {
+    const ATTN_LDS char* sp = stg + 2 * QT + 128 * sb + 16 * h;
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       lv[g4] = *(const ATTN_LDS f32x4*)(sp + 32 * g4);
-      dl[g4] = *(const ATTN_LDS f32x4*)(sp + 256 + 32 * g4);
+      const f32x4 d = *(const ATTN_LDS f32x4*)(sp + 256 + 32 * g4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dp[4 * g4 + e] = d[e];
     }
   };
-  // transposed A operands of dV^T (dO) and dK^T (Q): per (t, db) four reads
-  auto read_g = [&](const ATTN_LDS char* stage, int sb, i16x4 (&f)[8 * DB]) {
-    const ATTN_LDS char* ta = stage + tra_base + 512 * sb;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int o = 4 * db * CSTR + 256 * t, x = 4 * (DB * t + db);
-        f[x] = lds_read_tr16(ta + T::QT + o);
-        f[x + 1] = lds_read_tr16(ta + T::QT + o + 128);
-        f[x + 2] = lds_read_tr16(ta + o);
-        f[x + 3] = lds_read_tr16(ta + o + 128);
-      }
-  };
-  // S and dP: C[query][key], lane = key, register r = query 8(r/4) + 4h + r%4
-  auto mfma_s = [&](const bf16x8 (&f)[2 * KK], f32x16& s, f32x16& dp) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      s[r] = 0.0f;
-      dp[r] = 0.0f;
-    }
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      s = mfma32(f[2 * kk], kf[kk], s);
-      dp = mfma32(f[2 * kk + 1], vf[kk], dp);
-    }
-  };
-  // P and dS of a 32-query block, packed to bf16 in query order
-  auto softmax = [&](auto masked_t, int qb0, const f32x16& s, const f32x16& dp,
-                     const f32x4 (&lv)[4], const f32x4 (&dl)[4], uint32_t (&pk)[8],
-                     uint32_t (&dsk)[8]) {
+  // Stages rotate over three LDS slots: cur (this step), nxt (step i+1,
+  // loaded), fre (read by step i-1, receives step i+2).
+  // op holds the operands of the step's first LA products, lva/dpa block A's
+  // L2 and -Delta, on entry; the next step's on exit.
+  auto step = [&](auto masked_t, int i, const ATTN_LDS char* cur, const ATTN_LDS char* nxt,
+                  ATTN_LDS char* fre, bf16x8 (&op)[LA], f32x4 (&lva)[4], f32x16& dpa)
+      __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked_t)::value;
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      float pr[4], ds[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * g4 + e;
-        float v = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lv[g4][e]));
-        bool vis = kvalid;
-        if constexpr (MASKED) vis = vis && key <= qb0 + 8 * g4 + 4 * h + e;
-        v = vis ? v : 0.0f;
-        pr[e] = v;
-        ds[e] = v * (dp[r] - dl[g4][e]);
-      }
-      pk[2 * g4] = pack_bf16x2(pr[0], pr[1]);
-      pk[2 * g4 + 1] = pack_bf16x2(pr[2], pr[3]);
-      dsk[2 * g4] = pack_bf16x2(ds[0], ds[1]);
-      dsk[2 * g4 + 1] = pack_bf16x2(ds[2], ds[3]);
-    }
-  };
-  // dV^T += dO^T P, dK^T += Q^T dS
-  auto mfma_g = [&](const i16x4 (&f)[8 * DB], const uint32_t (&pk)[8], const uint32_t (&dsk)[8]) {
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const u32x4 pw = {pk[4 * t], pk[4 * t + 1], pk[4 * t + 2], pk[4 * t + 3]};
-      const u32x4 sw4 = {dsk[4 * t], dsk[4 * t + 1], dsk[4 * t + 2], dsk[4 * t + 3]};
-      const bf16x8 bp = __builtin_bit_cast(bf16x8, pw);
-      const bf16x8 bs = __builtin_bit_cast(bf16x8, sw4);
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int x = 4 * (DB * t + db);
-        dv[db] = mfma32(cat_tr(f[x], f[x + 1]), bp, dv[db]);
-        dk[db] = mfma32(cat_tr(f[x + 2], f[x + 3]), bs, dk[db]);
-      }
-    }
-  };
-
-  // One step: queries qfirst + 64i .. +63 as blocks A (first 32) and B, in
-  // four regions that keep the matrix core fed from one wave:
-  //   R1  S, dP of A                        reads: S/dP operands of B, stats of A
-  //   R2  S, dP of B      + P, dS of A      reads: transposed operands of A, stats of B
-  //   R3  dV, dK of A     + P, dS of B      reads: transposed operands of B
-  //   --  every LDS read of this stage done, step i+1's loads landed: barrier
-  //   R4  dV, dK of B     + loads of step i+2 into this stage, S/dP operands
-  //                         of step i+1's block A
-  // fa holds block A's S/dP operands on entry and the next step's on exit.
-  constexpr int NG = 8 * DB;
-  auto step = [&](int i, auto masked_t, bf16x8 (&fa)[2 * KK]) __attribute__((always_inline)) {
-    const int st = i & 1;
+    constexpr int STAT_B = 2;  // block B's statistics are read after this product
     const int q0 = qfirst + i * BQ;
-    const ATTN_LDS char* stage = stage_ptr(st);
-    bf16x8 fb[2 * KK];
-    f32x4 lva[4], dla[4], lvb[4], dlb[4];
-    i16x4 ga[NG], gb[NG];
-    f32x16 sa, dpa, sb, dpb;
-    uint32_t pka[8], dsa[8], pkb[8], dsb[8];
-    // R1
-    read_s(stage, 1, fb);
-    read_stats(stage, 0, lva, dla);
-    mfma_s(fa, sa, dpa);
-    __builtin_amdgcn_sched_barrier(0);
-    // R2
-    read_g(stage, 0, ga);
-    read_stats(stage, 1, lvb, dlb);
-    mfma_s(fb, sb, dpb);
-    softmax(masked_t, q0, sa, dpa, lva, dla, pka, dsa);
-    __builtin_amdgcn_sched_barrier(0);
-    // R3
-    read_g(stage, 1, gb);
-    mfma_g(ga, pka, dsa);
-    softmax(masked_t, q0 + 32, sb, dpb, lvb, dlb, pkb, dsb);
-    __builtin_amdgcn_sched_barrier(0);
-    wait_all();
+    bf16x8 o[NM + LA];
+    static_for(std::make_integer_sequence<int, LA>{}, [&](auto k) { o[k] = op[k]; });
+    f32x16 sacc[2], dacc[2];
+    dacc[0] = dpa;
+    f32x4 lvb[4];
+    uint32_t pk[2][8], dsk[2][8];
+    auto product = [&](auto m_t) __attribute__((always_inline)) {
+      constexpr int m = decltype(m_t)::value, ph = m / NP, j = m % NP;
+      if constexpr (ph < 2) {
+        if constexpr ((j & 1) == 0) {
+          if constexpr (j == 0) {
+            f32x16 z;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) z[r] = 0.0f;
+            sacc[ph] = mfma32(o[m], kf[0], z);
+          } else {
+            sacc[ph] = mfma32(o[m], kf[j >> 1], sacc[ph]);
+          }
+        } else {
+          dacc[ph] = mfma32(o[m], vf[j >> 1], dacc[ph]);
+        }
+      } else {
+        constexpr int sb = ph - 2, t = j / (2 * DB), db = (j / 2) % DB;
+        if constexpr ((j & 1) == 0) {
+          const u32x4 pw = {pk[sb][4 * t], pk[sb][4 * t + 1], pk[sb][4 * t + 2], pk[sb][4 * t + 3]};
+          dv[db] = mfma32(o[m], __builtin_bit_cast(bf16x8, pw), dv[db]);
+        } else {
+          const u32x4 sw = {dsk[sb][4 * t], dsk[sb][4 * t + 1], dsk[sb][4 * t + 2],
+                            dsk[sb][4 * t + 3]};
+          dk[db] = mfma32(o[m], __builtin_bit_cast(bf16x8, sw), dk[db]);
+        }
+      }
+    };
+    // softmax pair halves of block b (pair k: elements 2k, 2k+1 = query rows
+    // 8(k/2) + 4h + 2(k%2) + {0, 1} of the block): P = exp2(S c - L2) and
+    // dS = P (dP - Delta), packed to bf16 in query order.  Lanes of keys past
+    // S are left unmasked: a lane's P and dS feed only its own key's dK, dV
+    // columns, which are never stored.
+    float ex[2][8][2];
+    auto half0 = [&](auto b_t, auto k_t) __attribute__((always_inline)) {
+      constexpr int b = decltype(b_t)::value, k = decltype(k_t)::value, g4 = k / 2;
+      const f32x16& sv = sacc[b];
+      const f32x4(&lv)[4] = b ? lvb : lva;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        constexpr int e0 = 2 * (k % 2);
+        float v = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * k + u], c, -lv[g4][e0 + u]));
+        if constexpr (MASKED) v = key <= q0 + 32 * b + 8 * g4 + 4 * h + e0 + u ? v : 0.0f;
+        ex[b][k][u] = v;
+      }
+    };
+    auto half1 = [&](auto b_t, auto k_t) __attribute__((always_inline)) {
+      constexpr int b = decltype(b_t)::value, k = decltype(k_t)::value;
+      pk[b][k] = pack_bf16x2(ex[b][k][0], ex[b][k][1]);
+      dsk[b][k] = pack_bf16x2(ex[b][k][0] * dacc[b][2 * k], ex[b][k][1] * dacc[b][2 * k + 1]);
+    };
+    using Sl = BwdSlots<NP>;
+    static_assert(Sl::valid(), "softmax pairs must follow their scores and precede their use");
+    static_assert(Sl::slot(1, 7, 1) < NX, "block B's softmax must precede the barrier");
+    auto slot = [&](auto m_t) __attribute__((always_inline)) {
+      constexpr int m = decltype(m_t)::value;
+      product(m_t);
+      if constexpr (m < NX) {
+        if constexpr (m + LA < NM) o[m + LA] = operand(cur, std::integral_constant<int, m + LA>{});
+        if constexpr (m == STAT_B) read_stats(cur, 1, lvb, dacc[1]);
+      } else {
+        o[m + LA] = operand(nxt, std::integral_constant<int, m + LA - NM>{});
+        if constexpr (m == NX) read_stats(nxt, 0, lva, dpa);
+      }
+      static_for(std::make_integer_sequence<int, 2>{}, [&](auto b_t) {
+        static_for(std::make_integer_sequence<int, 8>{}, [&](auto k_t) {
+          constexpr int b = decltype(b_t)::value, k = decltype(k_t)::value;
+          if constexpr (Sl::slot(b, k, 0) == m) half0(b_t, k_t);
+          if constexpr (Sl::slot(b, k, 1) == m) half1(b_t, k_t);
+        });
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // ---- before the barrier: products 0 .. NX-1, reads of this stage
+    static_for(std::make_integer_sequence<int, NX>{}, slot);
+    // ---- step i+1's tiles have landed everywhere; stage fre is free
+    wait_vmcnt<0>();
     barrier();
-    // R4
-    fetch(i + 2, st);
-    read_s(stage_ptr(st ^ 1), 0, fa);
-    mfma_g(gb, pkb, dsb);
+    fetch(i + 2, fre);
     __builtin_amdgcn_sched_barrier(0);
+    // ---- after the barrier: products NX .. NM-1, reads of step i+1's head
+    static_for(std::make_integer_sequence<int, LA>{}, [&](auto k) {
+      slot(std::integral_constant<int, NX + decltype(k)::value>{});
+    });
+    static_for(std::make_integer_sequence<int, LA>{}, [&](auto k) { op[k] = o[NM + k]; });
   };
 
   using Yes = std::integral_constant<bool, true>;
   using No = std::integral_constant<bool, false>;
-  bf16x8 fa[2 * KK];
-  read_s(stage_ptr(0), 0, fa);
+  bf16x8 op[LA];
+  f32x4 lva[4];
+  f32x16 dpa;
+  static_for(std::make_integer_sequence<int, LA>{}, [&](auto k) { op[k] = operand(lds, k); });
+  read_stats(lds, 0, lva, dpa);
+  // stage rotation: offsets of cur, nxt, fre
+  int sc = 0, sn = T::STAGE, sf = 2 * T::STAGE;
+  auto rotate = [&]() {
+    const int t0 = sc;
+    sc = sn;
+    sn = sf;
+    sf = t0;
+  };
+  int i = 0;
   if constexpr (CAUSAL) {
     // keys k0 .. k0+127 against queries k0 .. k0+127: the only masked steps
-    step(0, Yes{}, fa);
-    if (nsteps > 1) step(1, Yes{}, fa);
-    for (int i = 2; i < nsteps; ++i) step(i, No{}, fa);
-  } else {
-    for (int i = 0; i < nsteps; ++i) step(i, No{}, fa);
+    for (; i < 2 && i < nsteps; ++i) {
+      step(Yes{}, i, lds + sc, lds + sn, lds + sf, op, lva, dpa);
+      rotate();
+    }
+  }
+  for (; i < nsteps; ++i) {
+    step(No{}, i, lds + sc, lds + sn, lds + sf, op, lva, dpa);
+    rotate();
   }
   wait_all();  // the loads of the (unused) steps past the end
 
@@ -356,14 +411,14 @@ void attn_bwd_main_kernel(BwdParams p) {
   if (kvalid) {
     uint16_t* dkr = p.dk + head + (size_t)key * D;
     uint16_t* dvr = p.dv + head + (size_t)key * D;
-    const float sc = p.scale;
+    const float sc2 = p.scale;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int d = 32 * db + 8 * g4 + 4 * h;
-        const u32x2 a = {pack_bf16x2(dk[db][4 * g4] * sc, dk[db][4 * g4 + 1] * sc),
-                         pack_bf16x2(dk[db][4 * g4 + 2] * sc, dk[db][4 * g4 + 3] * sc)};
+        const u32x2 a = {pack_bf16x2(dk[db][4 * g4] * sc2, dk[db][4 * g4 + 1] * sc2),
+                         pack_bf16x2(dk[db][4 * g4 + 2] * sc2, dk[db][4 * g4 + 3] * sc2)};
         const u32x2 b = {pack_bf16x2(dv[db][4 * g4], dv[db][4 * g4 + 1]),
                          pack_bf16x2(dv[db][4 * g4 + 2], dv[db][4 * g4 + 3])};
         *(u32x2*)(dkr + d) = a;

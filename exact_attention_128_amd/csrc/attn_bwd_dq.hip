@@ -124,7 +124,7 @@ void attn_bwd_dq_kernel(BwdParams p) {
     if (ok) {
       const float* st = p.stats + ((size_t)bh * p.nblk + (qrow >> 6)) * 128 + (qrow & 63);
       nl2 = -st[0];
-      dlt = st[64];
+      dlt = -st[64];
     }
   }
 

@@ -39,7 +39,7 @@ struct BwdParams {
   uint16_t* dk;
   uint16_t* dv;
   float* stats;   // workspace [B*H][nblk][2][64] fp32: per 64-row block, LSE*log2(e)
-                  // of each row, then Delta of each row (zero for rows past S)
+                  // of each row, then -Delta of each row (zero for rows past S)
   int bh;
   int S;
   int nblk;       // 64-row blocks per head, ceil(S / 64)

@@ -95,7 +95,7 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
 /*
  * Bytes of device workspace attn_bwd needs for this shape (0 if the shape is
  * invalid): two fp32 row statistics per query row, LSE_i * log2(e) and
- * Delta_i = sum_d dO_id * O_id, stored per 64-row block ([B][H][ceil(S/64)]
+ * -Delta_i = -sum_d dO_id * O_id, stored per 64-row block ([B][H][ceil(S/64)]
  * [2][64]), rounded up to 256 bytes.
  */
 size_t attn_bwd_workspace_size(int B, int H, int S, int D);
@@ -120,7 +120,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o,
 
 /* Phases of the backward, for attn_bwd_phases. */
 enum attn_bwd_phase {
-  ATTN_BWD_PRE = 1,   /* LSE*log2(e) and Delta = rowsum(dO * O) into the workspace */
+  ATTN_BWD_PRE = 1,   /* LSE*log2(e) and -Delta = -rowsum(dO * O) into the workspace */
   ATTN_BWD_MAIN = 2,  /* dK, dV written (reads the workspace)                      */
   ATTN_BWD_DQ = 4,    /* dQ written (reads the workspace)                          */
   ATTN_BWD_ALL = 7
