@@ -44,15 +44,15 @@ TRAFFIC_SOURCES = ("exact_attention_128_amd/csrc/attn_bwd.hip",
                    "exact_attention_128_amd/csrc/gfx950.h",
                    "exact_attention_128_amd/csrc/attn_internal.h",
                    "exact_attention_128_amd/build.py")
-TRAFFIC = {"workload": "bwd_causal_s4k", "read_bytes": 222961083, "write_bytes": 67144907,
-           "sources_sha256": "be60bf2f437b642d7b2c58bdb0ead01d27f73ba991bf35ac0b4b1ed8107cd7d0"}
+TRAFFIC = {"workload": "bwd_causal_s4k", "read_bytes": 230571974, "write_bytes": 67108939,
+           "sources_sha256": "08b88606156b56b02144c1bdf55bde67d46420f2ef95f14af817bc050925a479"}
 # the same for the forward on the causal S=8192 workload
 # (profiles/fwd_causal_s8k_counters.md)
 FWD_TRAFFIC_SOURCES = ("exact_attention_128_amd/csrc/attn_fwd.hip",
                        "exact_attention_128_amd/csrc/gfx950.h",
                        "exact_attention_128_amd/csrc/attn_internal.h")
-FWD_TRAFFIC = {"workload": "fwd_causal_s8k", "read_bytes": 1359603838, "write_bytes": 136319061,
-               "sources_sha256": "f3a19ac47b68a4722587a23092eac2acd6233251ca3a01ccd1cf086e1d08ae17"}
+FWD_TRAFFIC = {"workload": "fwd_causal_s8k", "read_bytes": 1365191226, "write_bytes": 136314880,
+               "sources_sha256": "d0f009d4f535e56bd0c13e98c36ba855b175d8a935a32e877899903839225cca"}
 
 
 def measured_traffic(workload, record=None, sources=None):
