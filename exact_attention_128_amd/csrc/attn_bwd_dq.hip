@@ -293,7 +293,13 @@ void attn_bwd_dq_kernel(BwdParams p) {
   fetch(0, 0);
   if (ntiles > 1) fetch(1, 1);
   if (ntiles > 2) fetch(2, 2);
-  sync_data(0);
+  // A full vmcnt(0) here, visible to the compiler, also retires the Q/dO row
+  // loads: the compiler cannot count the direct-to-LDS loads issued as
+  // inline assembly, so after a partial wait it would take some row loads as
+  // possibly still in flight and re-insert a vmcnt(0) inside every matrix
+  // half of the loop, stalling it on the tile loads of the same step.
+  wait_vmcnt<0>();
+  sync();
   uint32_t pk[2][8];     // dS^T of the tile whose dQ product comes next
   f32x16 sx[2], dpx[2];  // scores of the tile whose softmax comes next
   if (wtiles > 0) {
