@@ -206,8 +206,7 @@ void attn_fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[i][r] = 0.0f;
   float m_run = 0.0f;        // stale row max in log2 units (scores * c); set by step 0
-  float l_b = 0.0f;          // sum of bf16-rounded P (normalises O)
-  float l_f = 0.0f;          // sum of fp32 P (for the LSE)
+  float l_f = 0.0f;          // sum of fp32 P: normalises O and gives the LSE
   const float c = p.c;
   const float thresh = p.thresh;   // 2^tau
 
@@ -243,20 +242,28 @@ void attn_fwd_kernel(FwdParams p) {
   // products by scheduling groups, so each product finds its operands LA
   // products ahead: LDS latency stays hidden without holding a whole tile in
   // registers.
-  auto mphase = [&](int ks, int vs, f32x16 (&s)[4], const uint32_t (&pk)[4][8]) {
-    constexpr int NQ = 4 * KK, NP = 8 * DB, NM = NQ + NP, LA = 5;
+  // K fragment i of a step (the A operand of score product i)
+  auto kfrag = [&](const ATTN_LDS char* kb, int i) {
+    const int u = i / (2 * KK), kk = (i % (2 * KK)) >> 1, b = i & 1;
+    return lds_read_b128(kb + u * T::KSUB + 2 * kk * (BC * 16) + 32 * b * 16);
+  };
+  // The first LA K fragments of step st, read ahead of its matrix half (the
+  // half then starts with a product instead of waiting out an LDS read).
+  constexpr int LA = 5;
+  auto kpre_read = [&](int st, bf16x8 (&kp)[LA]) {
+    const ATTN_LDS char* kb = kslot(st) + kbase;
+#pragma unroll
+    for (int i = 0; i < LA; ++i) kp[i] = kfrag(kb, i);
+  };
+  auto mphase = [&](int ks, int vs, f32x16 (&s)[4], const uint32_t (&pk)[4][8],
+                    const bf16x8 (&kp)[LA]) {
+    constexpr int NQ = 4 * KK, NP = 8 * DB, NM = NQ + NP;
     const ATTN_LDS char* kb = kslot(ks) + kbase;
     const ATTN_LDS char* vb = vslot(vs) + vbase;
     bf16x8 kf[NQ];
     i16x4 vf[2 * NP];
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk)
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-          kf[2 * KK * u + 2 * kk + b] =
-              lds_read_b128(kb + u * T::KSUB + 2 * kk * (BC * 16) + 32 * b * 16);
+    for (int i = 0; i < NQ; ++i) kf[i] = i < LA ? kp[i] : kfrag(kb, i);
 #pragma unroll
     for (int bt = 0; bt < 8; ++bt)
 #pragma unroll
@@ -284,7 +291,7 @@ void attn_fwd_kernel(FwdParams p) {
       const u32x4 aw = {a0[0], a0[1], a1[0], a1[1]};
       o[db] = mfma32(__builtin_bit_cast(bf16x8, aw), __builtin_bit_cast(bf16x8, pw), o[db]);
     }
-    MSched<NQ, NM, LA>::apply();
+    MSched<NQ, NM, LA, true>::apply();
   };
   // keys past the sequence end, and above the causal diagonal, get -inf
   auto mask = [&](int st, f32x16 (&s)[4]) {
@@ -317,22 +324,11 @@ void attn_fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) pk[i][j] = pack_bf16x2(e[i][2 * j], e[i][2 * j + 1]);
   };
-  // l_b += the rounded weights of a packed step (exact products by 1, fp32
-  // sum; eight partial sums so that the adds do not wait on one another)
-  auto sum_packed = [&](const uint32_t (&pk)[4][8]) {
-    float a[8] = {l_b, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) a[j] = add_bf16x2(pk[i][j], a[j]);
-    l_b = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
-  };
   auto rescale = [&](float alpha) {
 #pragma unroll
     for (int i = 0; i < DB; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
-    l_b *= alpha;
     l_f *= alpha;
   };
   // e = 2^(x - mx) for the kept exponents x; returns this lane's partial sum.
@@ -360,7 +356,7 @@ void attn_fwd_kernel(FwdParams p) {
   // check, so the rare path needs no recomputation of the scores: it moves
   // each row's m up by its largest x (a row whose x never went positive keeps
   // m), scales O and the sums down to match, and redoes the exponentials.
-  // Leaves the packed weights in pk and adds them into l_b.
+  // Leaves the packed weights in pk.
   auto softmax = [&](f32x16 (&s)[4], uint32_t (&pk)[4][8]) {
     const float nm = -m_run;
 #pragma unroll
@@ -378,7 +374,6 @@ void attn_fwd_kernel(FwdParams p) {
     }
     l_f += t;
     pack(e, pk);
-    sum_packed(pk);
   };
 
   // ---- prologue: K of steps 0..2 and V of step 0 requested; once K 0, K 1
@@ -410,25 +405,32 @@ void attn_fwd_kernel(FwdParams p) {
       for (int r = 0; r < 16; ++r) s[i][r] = __builtin_fmaf(s[i][r], c, nm);
     l_f = expo(s, 0.0f, e);
     pack(e, pk);
-    sum_packed(pk);
   }
 
   // ---- main loop over steps of 128 keys.  K of step j lives in K slot j % 3,
   //      V of step j in V slot j % 2.  Each wave's step j is its matrix half
   //      (S^T of step j+1, O^T += V^T P^T of step j), a barrier, its softmax
-  //      half (step j+1), and a barrier; waves 4..7 start one barrier late,
-  //      so on every SIMD one wave's matrix half, at raised priority, meets
-  //      the other's softmax half.
+  //      half (step j+1) followed by the reads of the first K fragments of
+  //      step j+2, and a barrier; waves 4..7 start one barrier late, so on
+  //      every SIMD one wave's matrix half, at raised priority, meets the
+  //      other's softmax half.  Global barriers 2j and 2j+1 close the matrix
+  //      halves of step j of waves 0..3 and 4..7.
   //      Loads: waves 0..3 request V of step j+1 at the top of their step j
   //      (into the slot step j-1 used, which every wave finished reading in
-  //      the barrier before) and wait for it at their second barrier, right
-  //      before anyone reads it.  Waves 4..7 request K of step j+3 at the top
-  //      of their step j (the slot of step j, whose scores every wave computed
-  //      a step earlier) and wait for K of step j+2 at their first barrier,
-  //      right before waves 0..3 read it.  A wave at its last step still runs
-  //      the score products of the (unused) next slot, so the matrix half has
-  //      a single code path.
-  if (grp == 1) sync();
+  //      the barrier before) and wait for it at their second barrier (2j+1),
+  //      before any wave reads it.  Waves 4..7 request K of step j+3 at the
+  //      top of their step j (the slot of step j, whose scores every wave
+  //      computed by barrier 2j) and wait for it at their second barrier
+  //      (2j+2), a step before the first reads of it (the fragments read
+  //      ahead by waves 0..3 after barrier 2j+2).  A wave at its last step
+  //      still runs the score products of the (unused) next slot, so the
+  //      matrix half has a single code path.
+  bf16x8 kp[LA];
+  kpre_read(1, kp);
+  if (grp == 1) {
+    wait_vmcnt<0>();   // K of step 2 too, before barrier 0
+    sync();
+  }
   for (int j = 0; j < nsteps; ++j) {
     if (grp == 0) {
       if (j + 1 < nsteps) fetch_v(j + 1);
@@ -438,28 +440,26 @@ void attn_fwd_kernel(FwdParams p) {
     f32x16 sn[4];
     if (j < wsteps) {
       __builtin_amdgcn_s_setprio(1);
-      mphase(j + 1, j, sn, pk);
+      mphase(j + 1, j, sn, pk, kp);
       __builtin_amdgcn_s_setprio(0);
-    }
-    if (grp == 1) {
-      if (j + 3 < nsteps) wait_vmcnt<KPW>();
-      else wait_vmcnt<0>();
     }
     sync();
     if (j + 1 < wsteps) {
       if (needs_mask(j + 1)) mask(j + 1, sn);
       softmax(sn, pk);
     }
-    if (grp == 0) wait_vmcnt<0>();
+    kpre_read(j + 2, kp);
+    wait_vmcnt<0>();
     sync();
   }
   if (grp == 0) sync();
 
-  // ---- epilogue: O = O / l (bf16), LSE = ln2 * (m + log2 l)
-  const float lb = halfwave_sum(l_b);
+  // ---- epilogue: O = O / l (bf16), LSE = ln2 * (m + log2 l).  l is the
+  //      fp32 sum of the weights; the products used them rounded to bf16,
+  //      which moves O by about 2^-9 / sqrt(keys) relative.
   const float lf = halfwave_sum(l_f);
   if (qrow < S) {
-    const float inv = 1.0f / lb;
+    const float inv = 1.0f / lf;
     uint16_t* orow = p.o + head + (size_t)qrow * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)

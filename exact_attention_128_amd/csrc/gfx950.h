@@ -37,12 +37,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, p);
 }
 
-// acc + lo(p) + hi(p) for a packed bf16 pair: exact products by 1.0, fp32 sum.
-__device__ __forceinline__ float add_bf16x2(uint32_t p, float acc) {
-  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p), one, acc, false);
-}
-
 // Value held by the lane in the other half of the wave (lane ^ 32), combined.
 __device__ __forceinline__ float halfwave_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -110,9 +104,10 @@ __device__ __forceinline__ u32x4 buffer_rsrc(const void* base, uint32_t nbytes) 
 
 // Scheduling groups for a matrix half: NQ score products (one 16-byte LDS read
 // each) then NM - NQ output products (two 8-byte transposing reads each).
-// The reads of the first LA products go first; after product i come the reads
+// The reads of the first LA products go first (none when PRE: the caller
+// read those operands before the half began); after product i come the reads
 // that product i + LA needs.
-template <int NQ, int NM, int LA>
+template <int NQ, int NM, int LA, bool PRE = false>
 struct MSched {
   static constexpr int need(int i) { return i < NQ ? i + 1 : NQ + 2 * (i - NQ + 1); }
   template <int I>
@@ -126,7 +121,7 @@ struct MSched {
     (step<I>(), ...);
   }
   static __device__ __forceinline__ void apply() {
-    __builtin_amdgcn_sched_group_barrier(0x100, need(LA - 1), 0);
+    if constexpr (!PRE) __builtin_amdgcn_sched_group_barrier(0x100, need(LA - 1), 0);
     all(std::make_integer_sequence<int, NM>{});
   }
 };
