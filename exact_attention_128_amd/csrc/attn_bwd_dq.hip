@@ -21,6 +21,7 @@
 //                 dQ^T += K^T dS^T for the CURRENT tile (A = K^T by the
 //                 transposing LDS read, B = dS^T straight from registers)
 //   softmax half  P = exp2(S c - LSE log2 e), dS = P (dP - Delta), packed bf16
+//                 (the dP^T accumulators start at -Delta)
 // Query rows sit on lanes, so LSE and Delta are one register each.
 //
 // LDS slot: K as [D/8 chunk columns][64 keys][16 B] with the chunk columns
@@ -102,9 +103,9 @@ void attn_bwd_dq_kernel(BwdParams p) {
   // ---- this lane's query row: Q' (Q with the sign of the scale folded in,
   //      so that the score multiplier cq is positive and a masked score of
   //      -inf gives P = 0) and dO as B operands (features 16kk + 8h .. +7),
-  //      -LSE*log2(e) and Delta (zero past S, which makes dS zero there)
+  //      -LSE*log2(e) and -Delta (zero past S, which makes dS zero there)
   bf16x8 qf[KK], df[KK];
-  float nl2 = 0.0f, dlt = 0.0f;
+  float nl2 = 0.0f, ndl = 0.0f;
   {
     const bool ok = qrow < S;
     const uint16_t* Qr = p.q + head + (size_t)qrow * D + 8 * h;
@@ -124,7 +125,7 @@ void attn_bwd_dq_kernel(BwdParams p) {
     if (ok) {
       const float* st = p.stats + ((size_t)bh * p.nblk + (qrow >> 6)) * 128 + (qrow & 63);
       nl2 = -st[0];
-      dlt = -st[64];
+      ndl = st[64];
     }
   }
 
@@ -167,6 +168,9 @@ void attn_bwd_dq_kernel(BwdParams p) {
   for (int i = 0; i < DB; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[i][r] = 0.0f;
+  f32x16 dinit;  // this lane's -Delta in every register: where dP^T - Delta starts
+#pragma unroll
+  for (int r = 0; r < 16; ++r) dinit[r] = ndl;
   const float c = p.cq;
 
   // Per-lane LDS offsets within a slot (each fragment adds a constant):
@@ -187,7 +191,7 @@ void attn_bwd_dq_kernel(BwdParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         s[b][r] = 0.0f;
-        dp[b][r] = 0.0f;
+        dp[b][r] = ndl;
       }
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
@@ -228,14 +232,13 @@ void attn_bwd_dq_kernel(BwdParams p) {
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[b][r] = 0.0f;
-        dp[b][r] = 0.0f;
-      }
+      for (int r = 0; r < 16; ++r) s[b][r] = 0.0f;
 #pragma unroll
     for (int i = 0; i < 2 * KK; ++i) s[i & 1] = mfma32(af[i], qf[i >> 1], s[i & 1]);
+    // dP^T - Delta: both chains start from the tuple of this lane's -Delta
 #pragma unroll
-    for (int i = 0; i < 2 * KK; ++i) dp[i & 1] = mfma32(af[2 * KK + i], df[i >> 1], dp[i & 1]);
+    for (int i = 0; i < 2 * KK; ++i)
+      dp[i & 1] = mfma32(af[2 * KK + i], df[i >> 1], i < 2 ? dinit : dp[i & 1]);
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
       const int bt = i / DB, db = i % DB;
@@ -264,18 +267,16 @@ void attn_bwd_dq_kernel(BwdParams p) {
         if (32 * b + 8 * (r >> 2) + (r & 3) > lim) s[b][r] = -INFINITY;
   };
   // dS^T = P^T (dP^T - Delta), P^T = exp2(S^T c - LSE log2 e), packed to bf16
-  // in key order (the B operand of dQ^T).  The exponent arguments and dP - Delta
-  // come first, then all exponentials, then the products: a consumer right
-  // behind its v_exp_f32 would stall on the transcendental's latency.
+  // in key order (the B operand of dQ^T); dp already holds dP^T - Delta.  The
+  // exponent arguments come first, then all exponentials, then the products:
+  // a consumer right behind its v_exp_f32 would stall on the transcendental's
+  // latency.
   auto softmax = [&](int tile, f32x16 (&s)[2], f32x16 (&dp)[2], uint32_t (&pk)[2][8]) {
     if (needs_mask(tile)) mask(tile, s);
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[b][r] = __builtin_fmaf(s[b][r], c, nl2);
-        dp[b][r] = dp[b][r] - dlt;
-      }
+      for (int r = 0; r < 16; ++r) s[b][r] = __builtin_fmaf(s[b][r], c, nl2);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int b = 0; b < 2; ++b)
