@@ -94,8 +94,8 @@ void attn_fwd_kernel(FwdParams p) {
   constexpr int KK = D / 16;     // MFMA steps over the head dimension
   constexpr int DB = D / 32;     // 32-row blocks of O^T
   constexpr int CH = T::CH;
-  constexpr int KPW = T::KPIECE / 4;   // K pieces per wave of waves 4..7
-  constexpr int VPW = T::VPIECE / 4;   // V pieces per wave of waves 0..3
+  constexpr int KPW = T::KPIECE / 4;   // K pieces per wave of the four that load a K tile
+  constexpr int VPW = T::VPIECE / 4;   // V pieces per wave of the four that load a V tile
   static_assert(T::KPIECE % 4 == 0 && T::VPIECE % 4 == 0, "pieces must split over 4 waves");
 
   __shared__ __attribute__((aligned(16))) char smem[T::LDS];  // [K ring][V ring]
@@ -163,8 +163,9 @@ void attn_fwd_kernel(FwdParams p) {
   const int wend = CAUSAL ? min(S, qw + 32) : S;
   const int wsteps = qw < S ? (wend + 2 * BC - 1) / (2 * BC) : 0;
 
-  // ---- K/V of a step: HBM -> LDS directly (rows past S read as zero).
-  //      Waves 4..7 move K, waves 0..3 move V.  Lane l of a K piece carries
+  // ---- K/V of a step: HBM -> LDS directly (rows past S read as zero), a
+  //      tile split over the four waves of one group (one wave per SIMD; the
+  //      schedule below says which group loads what).  Lane l of a K piece carries
   //      key l of one chunk column; lane l of a V piece carries 16 bytes of key
   //      l/4 of one feature block; every piece lands as one 1 KiB run.
   const u32x4 krs = buffer_rsrc(p.k + head, (uint32_t)S * D * 2);
@@ -173,22 +174,22 @@ void attn_fwd_kernel(FwdParams p) {
   const int vl_off = (lane >> 2) * (2 * D) + (lane & 3) * 16;
   ATTN_LDS char* const kring = (ATTN_LDS char*)smem;
   ATTN_LDS char* const vring = kring + T::NKS * T::KSLOT;
-  auto fetch_k = [&](int st) {   // waves 4..7
+  auto fetch_k = [&](int st) {
     const int key0 = st * 2 * BC;
     ATTN_LDS char* base = kring + (st % T::NKS) * T::KSLOT;
 #pragma unroll
     for (int k = 0; k < KPW; ++k) {
-      const int i = (w - 4) + 4 * k;
+      const int i = (w & 3) + 4 * k;
       const int u = i / CH, cc = i % CH;
       lds_dma16(base + u * T::KSUB + cc * 1024, krs, kl_off, (key0 + u * BC) * (2 * D) + cc * 16);
     }
   };
-  auto fetch_v = [&](int st) {   // waves 0..3
+  auto fetch_v = [&](int st) {
     const int key0 = st * 2 * BC;
     ATTN_LDS char* base = vring + (st % T::NVS) * T::VSLOT;
 #pragma unroll
     for (int k = 0; k < VPW; ++k) {
-      const int i = w + 4 * k;
+      const int i = (w & 3) + 4 * k;
       const int u = i / (DB * 4), r = i % (DB * 4), db = r >> 2, rg = r & 3;
       lds_dma16(base + u * T::VSUB + db * (BC * 64) + rg * 1024, vrs, vl_off,
                 (key0 + u * BC + 16 * rg) * (2 * D) + db * 64);
@@ -383,12 +384,11 @@ void attn_fwd_kernel(FwdParams p) {
     fetch_k(0);
     if (nsteps > 1) fetch_k(1);
     if (nsteps > 2) fetch_k(2);
-    if (nsteps > 2) wait_vmcnt<KPW>();
-    else wait_vmcnt<0>();
   } else {
     fetch_v(0);
-    wait_vmcnt<0>();
+    if (nsteps > 1) fetch_v(1);
   }
+  wait_vmcnt<0>();
   sync();
 
   uint32_t pk[4][8];
@@ -414,42 +414,40 @@ void attn_fwd_kernel(FwdParams p) {
   //      step j+2, and a barrier; waves 4..7 start one barrier late, so on
   //      every SIMD one wave's matrix half, at raised priority, meets the
   //      other's softmax half.  Global barriers 2j and 2j+1 close the matrix
-  //      halves of step j of waves 0..3 and 4..7.
-  //      Loads: waves 0..3 request V of step j+1 at the top of their step j
-  //      (into the slot step j-1 used, which every wave finished reading in
-  //      the barrier before) and wait for it at their second barrier (2j+1),
-  //      before any wave reads it.  Waves 4..7 request K of step j+3 at the
-  //      top of their step j (the slot of step j, whose scores every wave
-  //      computed by barrier 2j) and wait for it at their second barrier
-  //      (2j+2), a step before the first reads of it (the fragments read
-  //      ahead by waves 0..3 after barrier 2j+2).  A wave at its last step
+  //      halves of step j of waves 0..3 and 4..7 (barrier -1 ends the
+  //      prologue, which loads K of steps 0..2 and V of steps 0..1).
+  //      Loads are issued at the top of the softmax half, where the wave has
+  //      time to spare, and waited for at the end of its next matrix half:
+  //      waves 0..3 request K of step j+3 after barrier 2j (into the slot of
+  //      K of step j, whose last reads end at barrier 2j-1) and wait before
+  //      barrier 2j+2, the first reads of it coming after that barrier;
+  //      waves 4..7 request V of step j+2 after barrier 2j+1 (into the slot of
+  //      V of step j, whose last reads end at barrier 2j+1) and wait before
+  //      barrier 2j+3, after which it is first read.  A wave at its last step
   //      still runs the score products of the (unused) next slot, so the
   //      matrix half has a single code path.
   bf16x8 kp[LA];
   kpre_read(1, kp);
-  if (grp == 1) {
-    wait_vmcnt<0>();   // K of step 2 too, before barrier 0
-    sync();
-  }
+  if (grp == 1) sync();
   for (int j = 0; j < nsteps; ++j) {
-    if (grp == 0) {
-      if (j + 1 < nsteps) fetch_v(j + 1);
-    } else {
-      if (j + 3 < nsteps) fetch_k(j + 3);
-    }
     f32x16 sn[4];
     if (j < wsteps) {
       __builtin_amdgcn_s_setprio(1);
       mphase(j + 1, j, sn, pk, kp);
       __builtin_amdgcn_s_setprio(0);
     }
+    wait_vmcnt<0>();
     sync();
+    if (grp == 0) {
+      if (j + 3 < nsteps) fetch_k(j + 3);
+    } else {
+      if (j + 2 < nsteps) fetch_v(j + 2);
+    }
     if (j + 1 < wsteps) {
       if (needs_mask(j + 1)) mask(j + 1, sn);
       softmax(sn, pk);
     }
     kpre_read(j + 2, kp);
-    wait_vmcnt<0>();
     sync();
   }
   if (grp == 0) sync();
