@@ -157,11 +157,6 @@ void attn_bwd_dq_kernel(BwdParams p) {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
-  auto sync_data = [&](int k) {
-    if (k + 2 < ntiles) wait_vmcnt<NPW>();
-    else wait_vmcnt<0>();
-    sync();
-  };
 
   f32x16 o[DB];  // dQ^T: lane = query row, registers = features
 #pragma unroll
@@ -309,26 +304,34 @@ void attn_bwd_dq_kernel(BwdParams p) {
   }
 
   // ---- main loop: the forward's schedule.  Tile j lives in slot j % 4.
-  //      Each wave's step j is its matrix half (which first requests tile
-  //      j+3 into the slot tile j-1 used), a barrier, its softmax half, and a
-  //      barrier; waves 4..7 start one barrier late, so on every SIMD one
-  //      wave's matrix half (at raised priority) meets the other's softmax
-  //      half.  The barrier after which a wave next reads tile j+1 is the one
-  //      where it has waited for its own loads of that tile.
+  //      Each wave's step j is its matrix half, a barrier, its softmax half
+  //      (which first requests its pieces of tile j+3), and a barrier; waves
+  //      4..7 start one barrier late, so on every SIMD one wave's matrix half
+  //      (at raised priority) meets the other's softmax half.  Global
+  //      barriers 2j and 2j+1 end the matrix halves of step j of waves 0..3
+  //      and 4..7; tile m is read between barriers 2m-3 and 2m+1, so tile
+  //      j+3 may replace tile j-1 after barrier 2j-1 and must have landed by
+  //      barrier 2j+3.  Waves 0..3 request it after barrier 2j and wait for
+  //      it before barrier 2j+3 (the end of their next softmax half); waves
+  //      4..7 request it after barrier 2j+1 and wait before barrier 2j+3 (the
+  //      end of their next matrix half).
   const int grp = w >> 2;
   if (grp == 1) sync();
   for (int j = 0; j < ntiles; ++j) {
-    if (j + 3 < ntiles) fetch(j + 3, (j + 3) & (NS - 1));
     if (j < wtiles) {
       __builtin_amdgcn_s_setprio(1);
       mphase((j + 1) & (NS - 1), j & (NS - 1), sx, dpx, pk);
       __builtin_amdgcn_s_setprio(0);
     }
-    if (grp == 0) sync();
-    else sync_data(j + 1);
+    if (grp == 1) wait_vmcnt<0>();   // tile j+2, requested in the previous step
+    sync();
+    if (j + 3 < ntiles) fetch(j + 3, (j + 3) & (NS - 1));
     if (j + 1 < wtiles) softmax(j + 1, sx, dpx, pk);
-    if (grp == 0) sync_data(j + 1);
-    else sync();
+    if (grp == 0) {   // tile j+2, requested in the previous step
+      if (j + 3 < ntiles) wait_vmcnt<NPW>();
+      else wait_vmcnt<0>();
+    }
+    sync();
   }
   if (grp == 0) sync();
 
