@@ -8,8 +8,10 @@
 // three products dQ needs in a kernel of its own.
 //
 // Two kernels here, on the caller's stream (dQ is computed by the kernel of
-// attn_bwd_dq.hip, which owns query rows and needs no atomics):
-//   pre    per 64-row block of each head: L2_i = LSE_i * log2(e) and
+// attn_bwd_dq.hip, which owns query rows, needs no atomics and runs first: it
+// also writes the row statistics that the main kernel reads):
+//   pre    the row statistics alone, for callers that want them without dQ:
+//          per 64-row block of each head, L2_i = LSE_i * log2(e) and
 //          -Delta_i = -sum_d dO_id * O_id (fp32, from the bf16 O), zero for
 //          the padding rows past S
 //   main   dK, dV: one workgroup per (head, 128-key block); each of its 4 waves
@@ -20,9 +22,9 @@
 //          (the dP accumulator starts at -Delta, so dS is a single product)
 //            dV^T += dO^T P,  dK^T += Q^T dS   (P, dS straight from registers)
 //
-// Memory pipeline.  Q, dO and the (L2, Delta) block of step i+1 travel from
-// HBM straight into LDS (buffer loads with the LDS destination bit) while step
-// i computes; two LDS stages, one barrier per step.  The Q/dO tiles are
+// Memory pipeline.  Q, dO and the (L2, -Delta) block of a step travel from
+// HBM straight into LDS (buffer loads with the LDS destination bit) two steps
+// ahead; three LDS stages, one barrier per step.  The Q/dO tiles are
 // stored as [D/8 chunk columns][64 rows][16 bytes] with the chunk columns 64
 // bytes apart mod 256, so both fragment reads are free of bank conflicts: the
 // 16-byte reads of the score products (32 rows of one chunk column per half
@@ -431,13 +433,19 @@ template <int D, bool CAUSAL>
 static hipError_t launch_bwd_t(const BwdParams& p0, unsigned phases, hipStream_t stream) {
   BwdParams p = p0;
   hipError_t e = hipSuccess;
-  if (phases & 1u) {
+  // the dQ kernel writes the row statistics itself: the separate kernel runs
+  // only for callers that ask for them without dQ
+  if ((phases & 1u) && !(phases & 4u)) {
     const long rows_pad = (long)p.bh * p.nblk * 64;
     const long threads = rows_pad * (D / 8);
     const long grid = (threads + 255) / 256;
     void* args[] = {&p, (void*)&rows_pad};
     e = hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_pre_kernel<D>),
                         dim3((unsigned)grid), dim3(256), args, 0, stream);
+    if (e != hipSuccess) return e;
+  }
+  if (phases & 4u) {
+    e = launch_bwd_dq(p, D, CAUSAL, stream);
     if (e != hipSuccess) return e;
   }
   if (phases & 2u) {
@@ -449,7 +457,6 @@ static hipError_t launch_bwd_t(const BwdParams& p0, unsigned phases, hipStream_t
                         dim3((unsigned)grid), dim3(256), args, 0, stream);
     if (e != hipSuccess) return e;
   }
-  if (phases & 4u) e = launch_bwd_dq(p, D, CAUSAL, stream);
   return e;
 }
 

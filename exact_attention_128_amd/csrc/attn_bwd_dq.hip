@@ -6,7 +6,9 @@
 // computed per query block, walking the key/value sequence like the forward:
 // the probabilities are recomputed from the forward's LSE (the recomputation
 // lever of the Tencent Cloud article "AI Infra 系列 第六章 GPU 性能工程（二）",
-// section 5), so no row statistic moves and no softmax rescale is needed.
+// section 5), so no softmax rescale is needed.  Each query row's Delta is
+// formed here from its O and dO rows, and the row statistics (LSE log2 e,
+// -Delta) go to the workspace for the dK/dV kernel, which runs after this one.
 // Owning the query rows makes dQ a plain register accumulation: no atomics,
 // and the result is deterministic.  (fp32 atomics from the key-block kernel
 // would cost more than these three recomputed products on MI355X, whose L2
@@ -103,29 +105,44 @@ void attn_bwd_dq_kernel(BwdParams p) {
   // ---- this lane's query row: Q' (Q with the sign of the scale folded in,
   //      so that the score multiplier cq is positive and a masked score of
   //      -inf gives P = 0) and dO as B operands (features 16kk + 8h .. +7),
-  //      -LSE*log2(e) and -Delta (zero past S, which makes dS zero there)
+  //      -LSE*log2(e) and -Delta, Delta = sum_d dO_d O_d in fp32 from the
+  //      bf16 O (zero past S, which makes dS zero there).  The row statistics
+  //      also go to the workspace ([B*H][nblk][L2 x 64, -Delta x 64]), where
+  //      the dK/dV kernel reads them; rows past S inside the last 64-row
+  //      block get zeros there.
   bf16x8 qf[KK], df[KK];
   float nl2 = 0.0f, ndl = 0.0f;
   {
     const bool ok = qrow < S;
     const uint16_t* Qr = p.q + head + (size_t)qrow * D + 8 * h;
-    const uint16_t* Or = p.dout + head + (size_t)qrow * D + 8 * h;
+    const uint16_t* Dr = p.dout + head + (size_t)qrow * D + 8 * h;
+    const uint16_t* Or = p.o + head + (size_t)qrow * D + 8 * h;
+    float dsum = 0.0f;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+      u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u}, ov = {0u, 0u, 0u, 0u};
       if (ok) {
         a = *(const u32x4*)(Qr + 16 * kk);
-        b = *(const u32x4*)(Or + 16 * kk);
+        b = *(const u32x4*)(Dr + 16 * kk);
+        ov = *(const u32x4*)(Or + 16 * kk);
       }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) a[e] = (a[e] ^ p.qxor) & p.qand;
+      for (int e = 0; e < 4; ++e) {
+        dsum = __builtin_fmaf(__uint_as_float(b[e] << 16), __uint_as_float(ov[e] << 16), dsum);
+        dsum = __builtin_fmaf(__uint_as_float(b[e] & 0xffff0000u),
+                              __uint_as_float(ov[e] & 0xffff0000u), dsum);
+        a[e] = (a[e] ^ p.qxor) & p.qand;
+      }
       qf[kk] = __builtin_bit_cast(bf16x8, a);
       df[kk] = __builtin_bit_cast(bf16x8, b);
     }
-    if (ok) {
-      const float* st = p.stats + ((size_t)bh * p.nblk + (qrow >> 6)) * 128 + (qrow & 63);
-      nl2 = -st[0];
-      ndl = st[64];
+    const float l2 = ok ? p.lse[(size_t)bh * S + qrow] * kLog2e : 0.0f;
+    ndl = -halfwave_sum(dsum);
+    nl2 = -l2;
+    if (h == 0 && qrow < p.nblk * 64) {
+      float* st = p.stats + ((size_t)bh * p.nblk + (qrow >> 6)) * 128 + (qrow & 63);
+      st[0] = l2;
+      st[64] = ndl;
     }
   }
 

@@ -109,9 +109,10 @@ size_t attn_bwd_workspace_size(int B, int H, int S, int D);
  *   workspace    device memory of at least attn_bwd_workspace_size(B,H,S,D)
  *                bytes, 256-byte aligned, owned by the caller; its contents
  *                on entry do not matter and are garbage on return.
- * Every output is deterministic (no atomics).  Enqueues three kernels on
- * `stream`: the row statistics, dK/dV (one workgroup per 128-key block), and
- * dQ (one workgroup per 256-row query block).
+ * Every output is deterministic (no atomics).  Enqueues two kernels on
+ * `stream`: dQ (one workgroup per 256-row query block), which also writes the
+ * row statistics into the workspace, then dK/dV (one workgroup per 128-key
+ * block), which reads them.
  */
 int attn_bwd(const void* q, const void* k, const void* v, const void* o,
              const float* lse, const void* dout, void* dq, void* dk, void* dv,
@@ -122,15 +123,16 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o,
 enum attn_bwd_phase {
   ATTN_BWD_PRE = 1,   /* LSE*log2(e) and -Delta = -rowsum(dO * O) into the workspace */
   ATTN_BWD_MAIN = 2,  /* dK, dV written (reads the workspace)                      */
-  ATTN_BWD_DQ = 4,    /* dQ written (reads the workspace)                          */
+  ATTN_BWD_DQ = 4,    /* dQ written; writes the same statistics as PRE             */
   ATTN_BWD_ALL = 7
 };
 
 /*
  * attn_bwd restricted to the phases set in `phases` (a nonzero subset of
- * ATTN_BWD_ALL), enqueued in the order PRE, MAIN, DQ.  MAIN and DQ read the
- * statistics PRE left in `workspace` (for the same o, lse, dout), and are
- * independent of each other.  For callers that time or schedule the phases
+ * ATTN_BWD_ALL), enqueued in the order PRE, DQ, MAIN; PRE is skipped when DQ
+ * is requested, since DQ writes the same statistics.  MAIN reads the
+ * statistics that PRE or DQ left in `workspace` (for the same o, lse, dout),
+ * also from an earlier call.  For callers that time or schedule the phases
  * separately; arguments otherwise as attn_bwd.
  * phases == 0 or outside ATTN_BWD_ALL: ATTN_ERR_UNSUPPORTED.
  */

@@ -80,6 +80,42 @@ def test_non_default_stream():
     P.assert_grads_ok(P.grad_errors(got, ref), "side stream")
 
 
+def test_phase_subsets():
+    """attn_bwd_phases: DQ writes the row statistics itself, so DQ then MAIN
+    (on a workspace filled with garbage) reproduces the whole backward bit for
+    bit; PRE then MAIN gives the same dK, dV up to the summation order of
+    Delta, both against the oracle."""
+    import torch
+    import exact_attention_128_amd as A
+    B, H, S, D = 1, 3, 300, 128
+    bits = ai.make_inputs(B, H, S, D, 43, with_dout=True)
+    scale = 1.0 / np.sqrt(D)
+    dev = torch.device("cuda", 0)
+    q, k, v, do = (ai.to_torch_bf16(bits[n], dev) for n in ("q", "k", "v", "do"))
+    o, lse = A.fwd(q, k, v, causal=True, scale=scale)
+    n = A.bwd_workspace_size(B, H, S, D)
+
+    def run(*phase_list):
+        ws = torch.full((n,), 0x7f, dtype=torch.uint8, device=dev)   # garbage
+        outs = [torch.full_like(q, float("nan")) for _ in range(3)]
+        for ph in phase_list:
+            A.bwd_out(q, k, v, o, lse, do, *outs, ws, causal=True, scale=scale, phases=ph)
+        torch.cuda.synchronize()
+        return [ai.bf16_bits_to_f64(ai.torch_bf16_to_bits(t)) for t in outs]
+
+    full = run(A.BWD_ALL)
+    split = run(A.BWD_DQ, A.BWD_MAIN)
+    for a_, b_ in zip(full, split):
+        assert np.array_equal(a_, b_)
+    pre = run(A.BWD_PRE, A.BWD_MAIN)
+    ref = P.oracle_bwd_heads(bits, True, scale, range(B * H))
+    ref = tuple(np.stack([ref[hd][i] for hd in range(B * H)]).reshape(B, H, S, D)
+                for i in range(3))
+    err = P.grad_errors((full[0], pre[1], pre[2]), ref)
+    P.assert_grads_ok(err, "PRE then MAIN")
+    assert np.isnan(pre[0]).all()   # dQ not requested: left untouched
+
+
 def test_many_heads():
     err, _ = _case(3, 50, 160, 128, True, seed=32)
     P.assert_grads_ok(err, "many heads")
