@@ -44,14 +44,14 @@ TRAFFIC_SOURCES = ("exact_attention_128_amd/csrc/attn_bwd.hip",
                    "exact_attention_128_amd/csrc/gfx950.h",
                    "exact_attention_128_amd/csrc/attn_internal.h",
                    "exact_attention_128_amd/build.py")
-TRAFFIC = {"workload": "bwd_causal_s4k", "read_bytes": 225971172, "write_bytes": 67130485,
-           "sources_sha256": "e0b8ae4a93de9947ac6feb38795d101f29781e332dd0c02e426a531a91416ad4"}
+TRAFFIC = {"workload": "bwd_causal_s4k", "read_bytes": 225076134, "write_bytes": 67108907,
+           "sources_sha256": "608d7df4e487c4041ee44a8e12f82af53ce6cfe5fa78ebb432333ee5d1afebc1"}
 # the same for the forward on the causal S=8192 workload
 # (profiles/fwd_causal_s8k_counters.md)
 FWD_TRAFFIC_SOURCES = ("exact_attention_128_amd/csrc/attn_fwd.hip",
                        "exact_attention_128_amd/csrc/gfx950.h",
                        "exact_attention_128_amd/csrc/attn_internal.h")
-FWD_TRAFFIC = {"workload": "fwd_causal_s8k", "read_bytes": 1349305295, "write_bytes": 136316800,
+FWD_TRAFFIC = {"workload": "fwd_causal_s8k", "read_bytes": 1365182890, "write_bytes": 136314880,
                "sources_sha256": "6d9361e82af186fe8c4c31d1de74bde20d1d60e37856613d34fe7cf8bedcb65f"}
 
 
