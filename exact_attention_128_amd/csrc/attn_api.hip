@@ -72,7 +72,7 @@ extern "C" {
 
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
              int S, int D, float scale, int causal, attn_stream_t stream) {
-  return fwd_impl(q, k, v, o, lse, B, H, S, D, scale, causal, 8.0f, stream);
+  return fwd_impl(q, k, v, o, lse, B, H, S, D, scale, causal, 32.0f, stream);
 }
 
 int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,

@@ -70,9 +70,11 @@ enum attn_status {
  *   scale    multiplies the logits before masking and softmax (usually 1/sqrt(D)).
  *   causal   nonzero: key j is visible to query i iff j <= i.
  * The online softmax rescales the running output only when a row's maximum
- * grows by more than 8 (log2 units) over the stale maximum it is using, the
- * conditional-rescaling idea of FA4 (Tencent Cloud article, section 7); the
- * result is the same, see attn_fwd_ex.
+ * grows by more than 32 (log2 units) over the stale maximum it is using, the
+ * conditional-rescaling idea of FA4 (Tencent Cloud article, section 7): the
+ * unnormalised weights stay below 2^32, far inside the fp32 and bf16 exponent
+ * range of the sums and the PV product.  The result is the same for every
+ * threshold, see attn_fwd_ex.
  * Returns ATTN_OK or an attn_status code; nothing is written on error.
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,

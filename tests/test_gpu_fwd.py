@@ -61,11 +61,11 @@ def test_rescale_threshold_gives_same_result():
     o_ref, lse_ref = P.oracle_fwd_full(bits, True, scale)
     vmax = np.abs(ai.bf16_bits_to_f64(bits["v"])).max(axis=(2, 3), keepdims=True)
     outs = {}
-    for tau in (0.0, 8.0, 20.0):
+    for tau in (0.0, 8.0, 20.0, 32.0, 64.0):
         o, lse, _ = P.gpu_fwd(bits, True, scale, rescale_log2=tau)
         P.assert_fwd_ok(P.fwd_errors(o, lse, o_ref, lse_ref), "tau=%g" % tau)
         outs[tau] = o
-    for tau in (8.0, 20.0):
+    for tau in (8.0, 20.0, 32.0, 64.0):
         diff = np.abs(outs[tau] - outs[0.0])
         bound = 2 * 2.0 ** -8 * vmax + 2 * P.bf16_ulp(o_ref)
         assert np.all(diff <= bound), "tau=%g vs 0: max diff %.3e" % (tau, diff.max())
