@@ -91,8 +91,9 @@ def main():
                     help="target CPU time for the oracle sample")
     ap.add_argument("--only", default=None,
                     help="profiling driver: run one workload's kernels --steps times after "
-                         "--warmup runs and exit (a workload name, or 'copy' for a plain "
-                         "1 GiB device copy that calibrates the HBM byte counters)")
+                         "--warmup runs and exit (a workload name, 'copy' for a plain "
+                         "1 GiB device copy that calibrates the HBM byte counters, or 'gemm' "
+                         "for the bf16 8192^3 library GEMM that calibrates the MFMA clock)")
     args = ap.parse_args()
     if args.only is not None:
         run_only(args)
@@ -204,6 +205,24 @@ def main():
                 name, ms, tf, 100 * tf / PEAK_BF16_TFLOPS, gbs))
             del lq, lk, lv, lo, ll
             torch.cuda.empty_cache()
+        # Context for the MFMA peak on this part: a plain vendor-library bf16 GEMM
+        # (hipBLASLt through torch.matmul, contiguous 8192^3 operands, fp32
+        # accumulate) timed the same way.  Not part of the attention path.
+        n = 8192
+        ga = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+        gb = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+        gc = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
+        for _ in range(3):
+            torch.matmul(ga, gb, out=gc)
+        ms = time_launches(lambda: torch.matmul(ga, gb, out=gc), n_rep)
+        tf = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+        legs["library_gemm"] = {"op": "torch.matmul bf16 8192x8192x8192 (hipBLASLt)",
+                                "ms": round(ms, 4), "tflops": round(tf, 1),
+                                "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+        log("library GEMM (hipBLASLt bf16 8192^3): %.4f ms  %.1f TFLOPS (%.1f%%)" % (
+            ms, tf, 100 * tf / PEAK_BF16_TFLOPS))
+        del ga, gb, gc
+        torch.cuda.empty_cache()
         c3 = legs["fwd_causal_s8k"]
         fwd_roof = {"kernel": "attn_fwd_kernel<128,causal>", "workload": "fwd_causal_s8k",
                     "bound": "mfma", "achieved": c3["tflops"], "peak": PEAK_BF16_TFLOPS,
@@ -277,6 +296,17 @@ def run_only(args):
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if args.only == "gemm":
+        n = 8192
+        ga = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+        gb = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+        gc = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
+        for _ in range(args.warmup + args.steps):
+            torch.matmul(ga, gb, out=gc)
+        torch.cuda.synchronize()
+        print("ran gemm: %d launches of a bf16 %d^3 library GEMM" % (args.warmup + args.steps, n),
+              flush=True)
+        return
     if args.only == "copy":
         n = 1 << 30
         src = torch.ones(n, dtype=torch.uint8, device=dev)
