@@ -54,6 +54,9 @@ def _bind(lib):
     lib.oracle_attn_bwd.argtypes = [_dp, _dp, _dp, _dp, ctypes.c_long, ctypes.c_long,
                                     ctypes.c_long, ctypes.c_long, ctypes.c_double,
                                     ctypes.c_int, _dp, _dp, _dp]
+    lib.oracle_attn_bwd_causal_tail.argtypes = [_dp, _dp, ctypes.c_long, _dp, _dp,
+                                                ctypes.c_long, ctypes.c_long, ctypes.c_double,
+                                                _dp, _dp, _dp]
     lib.oracle_max_threads.restype = ctypes.c_int
     lib.oracle_set_threads.argtypes = [ctypes.c_int]
     return lib
@@ -133,6 +136,25 @@ class Oracle:
             raise RuntimeError("oracle_attn_bwd_head failed (%d)" % rc)
         return outs[0], outs[1], outs[2], outs[3], lse
 
+    def attn_bwd_causal_tail(self, q_tail, do_tail, k, v, scale: float):
+        """Causal backward for the last n rows and keys of ONE head.
+
+        q_tail, do_tail [n,D] are rows S-n .. S-1; k, v [S,D] the whole head.
+        Returns (dQ, dK, dV) of rows / keys S-n .. S-1, each [n,D].
+        """
+        q_tail, do_tail, k, v = _f64(q_tail), _f64(do_tail), _f64(k), _f64(v)
+        n, D = q_tail.shape
+        S = k.shape[0]
+        if do_tail.shape != (n, D) or k.shape != (S, D) or v.shape != (S, D) or n > S:
+            raise ValueError("shape mismatch")
+        outs = [np.empty((n, D), dtype=np.float64) for _ in range(3)]
+        rc = self._lib.oracle_attn_bwd_causal_tail(_ptr(q_tail), _ptr(do_tail), n, _ptr(k),
+                                                   _ptr(v), S, D, float(scale), _ptr(outs[0]),
+                                                   _ptr(outs[1]), _ptr(outs[2]))
+        if rc:
+            raise RuntimeError("oracle_attn_bwd_causal_tail failed (%d)" % rc)
+        return outs[0], outs[1], outs[2]
+
     def attn_bwd(self, q, k, v, do, scale: float, causal: bool):
         """Backward over [B,H,S,D]: returns (dQ, dK, dV)."""
         q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
@@ -187,6 +209,10 @@ def attn_bwd_head(q, k, v, do, scale: float, causal: bool):
 
 def attn_bwd(q, k, v, do, scale: float, causal: bool):
     return default().attn_bwd(q, k, v, do, scale, causal)
+
+
+def attn_bwd_causal_tail(q_tail, do_tail, k, v, scale: float):
+    return default().attn_bwd_causal_tail(q_tail, do_tail, k, v, scale)
 
 
 def fwd_flops(B: int, H: int, S: int, D: int, causal: bool) -> float:

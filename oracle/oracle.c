@@ -258,3 +258,93 @@ int oracle_attn_bwd(const double* q, const double* k, const double* v,
   }
   return 0;
 }
+
+/*
+ * Causal backward restricted to the last n positions of ONE head (used to
+ * check the end of a sequence too long for a whole-head oracle).  With the
+ * causal mask, key j >= S-n is seen only by queries i >= j, all of them in
+ * the last n rows, so dK_j and dV_j of those keys need the forward of just
+ * those rows; dQ_i of those rows sums over every key j <= i.  Same
+ * definitions as oracle_attn_bwd_head, evaluated for these rows and keys.
+ *   q_tail[n][D], do_tail[n][D]  query and dO rows S-n .. S-1
+ *   k, v [S][D]                  all keys and values of the head
+ *   dq_tail, dk_tail, dv_tail [n][D]  gradients of rows / keys S-n .. S-1
+ * Returns 0, or -1 on a bad argument or allocation failure.
+ */
+int oracle_attn_bwd_causal_tail(const double* q_tail, const double* do_tail,
+                                long n, const double* k, const double* v,
+                                long S, long D, double scale, double* dq_tail,
+                                double* dk_tail, double* dv_tail) {
+  if (n <= 0 || n > S || D <= 0) return -1;
+  const long t0 = S - n;
+  double* o = (double*)malloc(sizeof(double) * (size_t)(n * D));
+  double* lse = (double*)malloc(sizeof(double) * (size_t)n);
+  double* delta = (double*)malloc(sizeof(double) * (size_t)n);
+  if (!o || !lse || !delta) {
+    free(o); free(lse); free(delta);
+    return -1;
+  }
+  int err = 0;
+  /* rows S-n .. S-1: forward, Delta_i and dQ_i over keys 0 .. i */
+#pragma omp parallel
+  {
+    double* s_buf = (double*)malloc(sizeof(double) * (size_t)S);
+    if (!s_buf) {
+#pragma omp atomic write
+      err = -1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (long r = 0; r < n; ++r) {
+        const long i = t0 + r;
+        const double* qi = q_tail + r * D;
+        const double* doi = do_tail + r * D;
+        fwd_one_row(qi, i, k, v, S, D, scale, 1, s_buf, o + r * D, lse + r);
+        double dl = 0.0;
+        for (long d = 0; d < D; ++d) dl += doi[d] * o[r * D + d];
+        delta[r] = dl;
+        double* dqi = dq_tail + r * D;
+        for (long d = 0; d < D; ++d) dqi[d] = 0.0;
+        for (long j = 0; j <= i; ++j) {
+          double dot = 0.0;
+          for (long d = 0; d < D; ++d) dot += qi[d] * k[j * D + d];
+          const double p = exp(scale * dot - lse[r]);
+          double dp = 0.0;
+          for (long d = 0; d < D; ++d) dp += doi[d] * v[j * D + d];
+          const double ds = p * (dp - delta[r]);
+          for (long d = 0; d < D; ++d) dqi[d] += ds * k[j * D + d];
+        }
+        for (long d = 0; d < D; ++d) dqi[d] *= scale;
+      }
+      free(s_buf);
+    }
+  }
+  /* keys S-n .. S-1: dK_j and dV_j over the queries i = j .. S-1 */
+  if (!err) {
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long c = 0; c < n; ++c) {
+      const long j = t0 + c;
+      const double* kj = k + j * D;
+      const double* vj = v + j * D;
+      double* dkj = dk_tail + c * D;
+      double* dvj = dv_tail + c * D;
+      for (long d = 0; d < D; ++d) { dkj[d] = 0.0; dvj[d] = 0.0; }
+      for (long r = c; r < n; ++r) {
+        const double* qi = q_tail + r * D;
+        const double* doi = do_tail + r * D;
+        double dot = 0.0;
+        for (long d = 0; d < D; ++d) dot += qi[d] * kj[d];
+        const double p = exp(scale * dot - lse[r]);
+        double dp = 0.0;
+        for (long d = 0; d < D; ++d) dp += doi[d] * vj[d];
+        const double ds = p * (dp - delta[r]);
+        for (long d = 0; d < D; ++d) {
+          dvj[d] += p * doi[d];
+          dkj[d] += ds * qi[d];
+        }
+      }
+      for (long d = 0; d < D; ++d) dkj[d] *= scale;
+    }
+  }
+  free(o); free(lse); free(delta);
+  return err;
+}

@@ -251,6 +251,25 @@ def pin_torch_autograd(orc):
         _close(dv, tv.grad.numpy(), 1e-11, "autograd dV causal=%s" % causal)
 
 
+def pin_causal_tail_autograd(orc):
+    """The causal tail backward (last n rows' dQ, last n keys' dK/dV) against
+    PyTorch CPU fp64 autograd of the whole head, sliced to those rows/keys;
+    n = S covers the whole head, n = 1 the last position alone."""
+    import torch
+    rng = np.random.default_rng(22)
+    S, D, scale = 37, 8, 0.35
+    q, k, v, do = (_rand(rng, S, D) for _ in range(4))
+    tq, tk, tv = (torch.from_numpy(x.copy()).requires_grad_(True) for x in (q, k, v))
+    out = torch.nn.functional.scaled_dot_product_attention(tq[None], tk[None], tv[None],
+                                                           is_causal=True, scale=scale)
+    out.backward(torch.from_numpy(do)[None])
+    for n in (1, 11, S):
+        dq, dk, dv = orc.attn_bwd_causal_tail(q[S - n:], do[S - n:], k, v, scale)
+        _close(dq, tq.grad.numpy()[S - n:], 1e-11, "tail dQ n=%d" % n)
+        _close(dk, tk.grad.numpy()[S - n:], 1e-11, "tail dK n=%d" % n)
+        _close(dv, tv.grad.numpy()[S - n:], 1e-11, "tail dV n=%d" % n)
+
+
 def pin_backward_invariants(orc):
     rng = np.random.default_rng(21)
     S, D = 24, 8
@@ -273,5 +292,5 @@ def pin_backward_invariants(orc):
 FORWARD_PINS = [pin_golden_forward, pin_constant_v, pin_causal_row0, pin_zero_q, pin_key_shift,
                 pin_permutation, pin_mpmath_bruteforce, pin_torch_sdpa, pin_rows_match_full]
 BACKWARD_PINS = [pin_golden_backward, pin_finite_differences, pin_torch_autograd,
-                 pin_backward_invariants]
+                 pin_causal_tail_autograd, pin_backward_invariants]
 ALL_PINS = FORWARD_PINS + BACKWARD_PINS

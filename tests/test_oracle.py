@@ -53,6 +53,12 @@ MUTANTS = [
      "const long i0 = causal ? j + 1 : 0;", 1),
     ("delta_from_dout_only", "dl += doi[d] * o[i * D + d];", "dl += doi[d] * doi[d];", 1),
     ("dk_uses_dout", "dkj[d] += ds * qi[d];", "dkj[d] += ds * doi[d];", 1),
+    ("tail_dq_skips_diagonal", "for (long j = 0; j <= i; ++j) {", "for (long j = 0; j < i; ++j) {",
+     1),
+    ("tail_dkdv_skips_diagonal", "for (long r = c; r < n; ++r) {",
+     "for (long r = c + 1; r < n; ++r) {", 1),
+    ("tail_p_scale_dropped", "const double p = exp(scale * dot - lse[r]);",
+     "const double p = exp(dot - lse[r]);", 0),
 ]
 
 
