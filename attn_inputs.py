@@ -15,11 +15,19 @@ unspecified FlashAttention-4 forward workload):
     so each row's running maximum keeps rising along the sequence;
   * everything is rounded to bf16 (round to nearest, ties to even) once,
     after construction.
+Very long sequences (hundreds of millions of elements per tensor) use
+``make_inputs_chunked``: the same N(0,1) -> bf16 recipe, but each tensor is
+cut into a fixed number of row chunks, chunk c of tensor t drawing from its
+own PCG64 stream (``SeedSequence(seed).spawn``, child t * chunks + c), so
+the chunks can be drawn by parallel threads with a result that does not
+depend on the thread count.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
 import math
+import os
 
 import numpy as np
 
@@ -67,10 +75,14 @@ WORKLOADS = {
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round fp32 to bf16, nearest-even; returns the uint16 bit patterns."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    nan = np.isnan(x)
-    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    u = x.view(np.uint32)
+    # u + 0x7FFF + lsb wraps in 32 bits only for NaN patterns, replaced below
+    r = (u >> 16) & np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += u
+    r >>= 16
     r = r.astype(np.uint16)
+    nan = np.isnan(x)
     if nan.any():
         r[nan] = 0x7FC0
     return r
@@ -105,6 +117,30 @@ def make_inputs(B: int, H: int, S: int, D: int, seed: int, stress: bool = False,
     if with_dout:
         out["do"] = f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32))
     return out
+
+
+def make_inputs_chunked(B: int, H: int, S: int, D: int, seed: int, with_dout: bool = False,
+                        chunks: int = 64, threads: int | None = None) -> dict:
+    """Q, K, V (and dO) as bf16 bit arrays [B,H,S,D], N(0,1), drawn chunk-wise
+    from independent streams (see the module docstring)."""
+    names = ["q", "k", "v"] + (["do"] if with_dout else [])
+    rows = B * H * S
+    bounds = [rows * c // chunks for c in range(chunks + 1)]
+    children = np.random.SeedSequence(seed).spawn(len(names) * chunks)
+    out = {n: np.empty((rows, D), dtype=np.uint16) for n in names}
+    if threads is None:
+        threads = min(16, len(os.sched_getaffinity(0)))
+
+    def fill(task):
+        t, c = divmod(task, chunks)
+        r0, r1 = bounds[c], bounds[c + 1]
+        rng = np.random.Generator(np.random.PCG64(children[task]))
+        x = rng.standard_normal((r1 - r0, D), dtype=np.float32)
+        out[names[t]][r0:r1] = f32_to_bf16_bits(x)
+
+    with concurrent.futures.ThreadPoolExecutor(max_workers=max(1, threads)) as ex:
+        list(ex.map(fill, range(len(names) * chunks)))
+    return {n: a.reshape(B, H, S, D) for n, a in out.items()}
 
 
 def workload_inputs(w: Workload) -> dict:
