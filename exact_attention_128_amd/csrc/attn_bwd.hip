@@ -185,9 +185,7 @@ void attn_bwd_main_kernel(BwdParams p) {
   const bool kvalid = key < S;
   const size_t head = (size_t)bh * S * D;
   const uint32_t hbytes = (uint32_t)S * D * 2;
-  const u32x4 qrs = buffer_rsrc(p.q + head, hbytes);
-  const u32x4 ors = buffer_rsrc(p.dout + head, hbytes);
-  const u32x4 srs = buffer_rsrc(p.stats + (size_t)bh * p.nblk * 128, (uint32_t)p.nblk * 512);
+  const float* const stats_h = p.stats + (size_t)bh * p.nblk * 128;
 
   const int qfirst = CAUSAL ? k0 : 0;  // queries before k0 see none of these keys
   const int nsteps = (S - qfirst + BQ - 1) / BQ;
@@ -201,13 +199,17 @@ void attn_bwd_main_kernel(BwdParams p) {
   const int row_off = lane * (2 * D);
   auto fetch = [&](int step, ATTN_LDS char* base) __attribute__((always_inline)) {
     const int q0 = qfirst + step * BQ;
+    const uint32_t off = (uint32_t)q0 * (2 * D);
+    const u32x4 qrs = buffer_rsrc_at(p.q + head, hbytes, off);
+    const u32x4 ors = buffer_rsrc_at(p.dout + head, hbytes, off);
+    const u32x4 srs = buffer_rsrc_at(stats_h, (uint32_t)p.nblk * 512, (uint32_t)(q0 / BQ) * 512);
 #pragma unroll
     for (int k = 0; k < CH / NW; ++k) {
       const int i = w + NW * k;
-      lds_dma16(base + i * CSTR, qrs, row_off, q0 * (2 * D) + i * 16);
-      lds_dma16(base + QT + i * CSTR, ors, row_off, q0 * (2 * D) + i * 16);
+      lds_dma16(base + i * CSTR, qrs, row_off, i * 16);
+      lds_dma16(base + QT + i * CSTR, ors, row_off, i * 16);
     }
-    lds_dma16(base + 2 * QT, srs, lane * 16, (q0 / BQ) * 512);
+    lds_dma16(base + 2 * QT, srs, lane * 16, 0);
   };
 
   // ---- the first two steps' tiles; K and V rows of this lane's key (B

@@ -153,20 +153,20 @@ void attn_bwd_dq_kernel(BwdParams p) {
 
   // ---- K/V tiles HBM -> LDS slot (keys past S read as zero): piece i < CH is
   //      K chunk column i, the rest V chunk columns; lane l carries key l.
-  const u32x4 krs = buffer_rsrc(p.k + head, (uint32_t)S * D * 2);
-  const u32x4 vrs = buffer_rsrc(p.v + head, (uint32_t)S * D * 2);
+  const uint32_t hbytes = (uint32_t)S * D * 2;
   const int row_off = lane * (2 * D);
   auto fetch = [&](int tile, int slot) {
-    const int key0 = tile * BC;
+    const uint32_t off = (uint32_t)(tile * BC) * (2 * D);
+    const u32x4 krs = buffer_rsrc_at(p.k + head, hbytes, off);
+    const u32x4 vrs = buffer_rsrc_at(p.v + head, hbytes, off);
     ATTN_LDS char* base = (ATTN_LDS char*)smem + slot * T::SLOT;
 #pragma unroll
     for (int k = 0; k < NPW; ++k) {
       const int i = w + NW * k;  // wave-uniform
       if (i < CH)
-        lds_dma16(base + i * CSTR, krs, row_off, key0 * (2 * D) + i * 16);
+        lds_dma16(base + i * CSTR, krs, row_off, i * 16);
       else
-        lds_dma16(base + T::KTILE + (i - CH) * (BC * 16), vrs, row_off,
-                  key0 * (2 * D) + (i - CH) * 16);
+        lds_dma16(base + T::KTILE + (i - CH) * (BC * 16), vrs, row_off, (i - CH) * 16);
     }
   };
   auto sync = [&]() {

@@ -7,13 +7,14 @@
 //
 // Work decomposition.  A workgroup of NW = 8 waves owns BR = 256 consecutive
 // query rows of one (batch, head); each wave owns 32 of them.  Waves w and
-// w+4 share a SIMD.  The workgroup walks the key/value sequence in tiles of
-// BC = 64 keys held in a four-slot LDS ring.
+// w+4 share a SIMD.  The workgroup walks the key/value sequence in steps of
+// 128 keys (two 64-key sub-tiles), K in a three-slot and V in a two-slot LDS
+// ring.
 //
-// Each tile step of a wave has two halves:
-//   matrix half   S^T = K Q^T for the NEXT tile (16 MFMAs) and O^T += V^T P^T
-//                 for the CURRENT tile (4*D/32 MFMAs), with their LDS fragment
-//                 reads interleaved a few products ahead;
+// Each step of a wave has two halves:
+//   matrix half   S^T = K Q^T for the NEXT step (4*D/16 MFMAs) and O^T +=
+//                 V^T P^T for the CURRENT step (8*D/32 MFMAs), with their LDS
+//                 fragment reads interleaved a few products ahead;
 //   softmax half  the exponentials of the next tile's scores, their sums, and
 //                 the bf16 packing of P.
 // Waves 4..7 run half a step behind waves 0..3 (ping-pong, the portable form
@@ -50,8 +51,8 @@
 //                   A = V^T fragments read with the transposing LDS load.
 //
 // K/V tiles travel from HBM straight into LDS (buffer loads with the LDS
-// destination bit: no staging registers, no LDS write instructions), three
-// tiles ahead of use.  The LDS tiles use blocked layouts in which every
+// destination bit: no staging registers, no LDS write instructions), K three
+// and V two steps ahead of use.  The LDS tiles use blocked layouts in which every
 // fragment read (and every tile write) is a contiguous 256-byte run per 16 or
 // 32 lanes -- free of bank conflicts (the conflict-avoidance lever of the
 // Tencent Cloud article, section 4) without swizzling -- and each lane reaches
@@ -59,8 +60,8 @@
 //   K  [D/8 chunk columns][64 keys][16 bytes]
 //   V  [D/32 feature blocks][64 keys][32 features]
 //
-// l is summed from the bf16-rounded P that the PV product consumes (so a row
-// dominated by one key normalises exactly), and separately in fp32 for the LSE.
+// l, which normalises O and gives the LSE, is the fp32 sum of P; the PV
+// product consumes P rounded to bf16.
 #include "attn_internal.h"
 #include "gfx950.h"
 
@@ -168,8 +169,9 @@ void attn_fwd_kernel(FwdParams p) {
   //      schedule below says which group loads what).  Lane l of a K piece carries
   //      key l of one chunk column; lane l of a V piece carries 16 bytes of key
   //      l/4 of one feature block; every piece lands as one 1 KiB run.
-  const u32x4 krs = buffer_rsrc(p.k + head, (uint32_t)S * D * 2);
-  const u32x4 vrs = buffer_rsrc(p.v + head, (uint32_t)S * D * 2);
+  const uint32_t hbytes = (uint32_t)S * D * 2;
+  const uint16_t* const Kh = p.k + head;
+  const uint16_t* const Vh = p.v + head;
   const int kl_off = lane * (2 * D);
   const int vl_off = (lane >> 2) * (2 * D) + (lane & 3) * 16;
   ATTN_LDS char* const kring = (ATTN_LDS char*)smem;
@@ -181,7 +183,8 @@ void attn_fwd_kernel(FwdParams p) {
     for (int k = 0; k < KPW; ++k) {
       const int i = (w & 3) + 4 * k;
       const int u = i / CH, cc = i % CH;
-      lds_dma16(base + u * T::KSUB + cc * 1024, krs, kl_off, (key0 + u * BC) * (2 * D) + cc * 16);
+      const u32x4 rs = buffer_rsrc_at(Kh, hbytes, (uint32_t)(key0 + u * BC) * (2 * D));
+      lds_dma16(base + u * T::KSUB + cc * 1024, rs, kl_off, cc * 16);
     }
   };
   auto fetch_v = [&](int st) {
@@ -191,8 +194,8 @@ void attn_fwd_kernel(FwdParams p) {
     for (int k = 0; k < VPW; ++k) {
       const int i = (w & 3) + 4 * k;
       const int u = i / (DB * 4), r = i % (DB * 4), db = r >> 2, rg = r & 3;
-      lds_dma16(base + u * T::VSUB + db * (BC * 64) + rg * 1024, vrs, vl_off,
-                (key0 + u * BC + 16 * rg) * (2 * D) + db * 64);
+      const u32x4 rs = buffer_rsrc_at(Vh, hbytes, (uint32_t)(key0 + u * BC + 16 * rg) * (2 * D));
+      lds_dma16(base + u * T::VSUB + db * (BC * 64) + rg * 1024, rs, vl_off, db * 64);
     }
   };
   auto sync = [&]() {

@@ -102,6 +102,16 @@ __device__ __forceinline__ u32x4 buffer_rsrc(const void* base, uint32_t nbytes) 
   return r;
 }
 
+// Descriptor over bytes [off, nbytes) of the array at base (empty when off >=
+// nbytes): a load through it starts at the array's byte off.  The kernels
+// put a tile's first row at off and only a within-row byte offset in the
+// load's scalar offset, so the descriptor's size bounds every lane's row by
+// the array's true end (rows past it read as zero) whether or not the
+// hardware counts the scalar offset in its range check.
+__device__ __forceinline__ u32x4 buffer_rsrc_at(const void* base, uint32_t nbytes, uint32_t off) {
+  return buffer_rsrc((const char*)base + off, off < nbytes ? nbytes - off : 0u);
+}
+
 // Scheduling groups for a matrix half: NQ score products (one 16-byte LDS read
 // each) then NM - NQ output products (two 8-byte transposing reads each).
 // The reads of the first LA products go first (none when PRE: the caller
