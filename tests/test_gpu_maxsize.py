@@ -1,0 +1,107 @@
+"""The longest sequence the library accepts at D = 128: S*D must stay below
+2^29 (one head's K/V slab is addressed with 32-bit byte offsets), so
+S = 2^22 - 1 keys (ragged against every tile size), causal, one head, in the
+launch configuration of every other call.
+
+No oracle can evaluate a whole head of this length, so the check has three
+parts:
+  * forward: O and LSE of sampled rows (start, tile and block edges, middle,
+    end, random rows) against the oracle's per-row forward;
+  * backward, both ends: with the causal mask, the first rows' dQ (and O)
+    depend only on the first keys, so they equal the full oracle of the
+    prefix; the last keys' dK/dV depend only on the last queries, and the
+    last rows' dQ on all keys before them: the oracle's causal tail backward
+    covers both;
+  * backward, whole sequence: sum_j dV_j = sum_i dO_i (each row of P sums to
+    one) and sum_j dK_j = 0 (each row of dS sums to zero), summed in fp64 on
+    the device.  The expected deviation from bf16 rounding of P, dS and the
+    outputs is about 1e-2 per feature; the bound is 0.5 against sums of
+    size ~2e3.
+Inputs: N(0,1) bf16 from make_inputs_chunked (seed 4711)."""
+import math
+import sys
+import time
+
+import numpy as np
+import pytest
+
+import attn_inputs as ai
+import oracle
+import parity as P
+
+pytestmark = pytest.mark.gpu
+
+S_MAX = (1 << 22) - 1
+D = 128
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _bits_rows(t, rows):
+    """fp64 values of selected rows of a bf16 [S, D] device tensor."""
+    import torch
+    idx = torch.as_tensor(np.asarray(rows, dtype=np.int64), device=t.device)
+    return ai.bf16_bits_to_f64(ai.torch_bf16_to_bits(t.index_select(0, idx)))
+
+
+def test_max_sequence_causal():
+    import torch
+    import exact_attention_128_amd as A
+    S, scale = S_MAX, 1.0 / math.sqrt(D)
+    t0 = time.time()
+    bits = ai.make_inputs_chunked(1, 1, S, D, 4711, with_dout=True)
+    _say("inputs %.1f s" % (time.time() - t0))
+    dev = torch.device("cuda", 0)
+    q, k, v, do = (ai.to_torch_bf16(bits[n], dev) for n in ("q", "k", "v", "do"))
+    _say("max-size case: B=1 H=1 S=%d D=%d causal, forward" % (S, D))
+    o, lse = A.fwd(q, k, v, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    _say("max-size case: backward")
+    dq, dk, dv = A.bwd(q, k, v, o, lse, do, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    _say("gpu done %.1f s" % (time.time() - t0))
+    for name, t in (("O", o), ("LSE", lse), ("dQ", dq), ("dK", dk), ("dV", dv)):
+        assert bool(torch.isfinite(t).all()), "%s has non-finite values" % name
+
+    o2, l2, dq2, dk2, dv2 = (t[0, 0] for t in (o, lse, dq, dk, dv))
+    kf = ai.bf16_bits_to_f64(bits["k"][0, 0])
+    vf = ai.bf16_bits_to_f64(bits["v"][0, 0])
+    qb, dob = bits["q"][0, 0], bits["do"][0, 0]
+
+    # forward, sampled rows
+    rows = P.sample_rows(1, 1, S, n_heads=1, n_rows=24, seed=4712, block=256)[0]
+    o_ref, lse_ref = oracle.attn_fwd_rows(ai.bf16_bits_to_f64(qb[rows]), rows, kf, vf, scale,
+                                          True)
+    lse_got = l2.index_select(0, torch.as_tensor(rows, device=dev)).double().cpu().numpy()
+    err = P.fwd_errors(_bits_rows(o2, rows), lse_got, o_ref, lse_ref)
+    _say("forward rows", err, "%.1f s" % (time.time() - t0))
+    P.assert_fwd_ok(err, "max-size forward")
+
+    # backward, first rows: the causal prefix is a problem of its own
+    n0 = 300
+    pre = oracle.attn_bwd_head(*(ai.bf16_bits_to_f64(bits[n][0, 0, :n0])
+                                 for n in ("q", "k", "v", "do")), scale, True)
+    err = {"dq": float(np.abs(_bits_rows(dq2, range(n0)) - pre[0]).max())}
+    _say("backward prefix", err)
+    P.assert_grads_ok(err, "max-size prefix")
+
+    # backward, last rows and keys
+    n1 = 48
+    tail = np.arange(S - n1, S)
+    ref = oracle.attn_bwd_causal_tail(ai.bf16_bits_to_f64(qb[tail]),
+                                      ai.bf16_bits_to_f64(dob[tail]), kf, vf, scale)
+    err = P.grad_errors([_bits_rows(t, tail) for t in (dq2, dk2, dv2)], ref)
+    _say("backward tail", err, "%.1f s" % (time.time() - t0))
+    P.assert_grads_ok(err, "max-size tail")
+
+    # backward, whole sequence
+    sum_dv = dv2.double().sum(0)
+    sum_do = do[0, 0].double().sum(0)
+    e_dv = float((sum_dv - sum_do).abs().max())
+    e_dk = float(dk2.double().sum(0).abs().max())
+    _say("sum dV - sum dO %.3e (|sum dO| max %.1f), sum dK %.3e" % (
+        e_dv, float(sum_do.abs().max()), e_dk))
+    assert e_dv <= 0.5 and e_dk <= 0.5
