@@ -44,15 +44,15 @@ TRAFFIC_SOURCES = ("exact_attention_128_amd/csrc/attn_bwd.hip",
                    "exact_attention_128_amd/csrc/gfx950.h",
                    "exact_attention_128_amd/csrc/attn_internal.h",
                    "exact_attention_128_amd/build.py")
-TRAFFIC = {"workload": "bwd_causal_s4k", "read_bytes": 225076134, "write_bytes": 67108907,
-           "sources_sha256": "608d7df4e487c4041ee44a8e12f82af53ce6cfe5fa78ebb432333ee5d1afebc1"}
+TRAFFIC = {"workload": "bwd_causal_s4k", "read_bytes": 229614928, "write_bytes": 67108864,
+           "sources_sha256": "ffa7a277de202f028ae2abf64cfb34dff70e6be120a95896f664e5361e02f341"}
 # the same for the forward on the causal S=8192 workload
 # (profiles/fwd_causal_s8k_counters.md)
 FWD_TRAFFIC_SOURCES = ("exact_attention_128_amd/csrc/attn_fwd.hip",
                        "exact_attention_128_amd/csrc/gfx950.h",
                        "exact_attention_128_amd/csrc/attn_internal.h")
-FWD_TRAFFIC = {"workload": "fwd_causal_s8k", "read_bytes": 1365182890, "write_bytes": 136314880,
-               "sources_sha256": "6d9361e82af186fe8c4c31d1de74bde20d1d60e37856613d34fe7cf8bedcb65f"}
+FWD_TRAFFIC = {"workload": "fwd_causal_s8k", "read_bytes": 1344340421, "write_bytes": 136317888,
+               "sources_sha256": "53288e5b7a021b1c7917e82f2caaf2e0ee6e048d2581d9a87da32cdd1530b587"}
 
 
 def measured_traffic(workload, record=None, sources=None):
