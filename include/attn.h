@@ -30,7 +30,10 @@
  *   - Arguments are validated on the host before any HIP call.  No C++
  *     exception crosses this boundary.  Calls are thread-safe and re-entrant.
  *   - Supported: B, H, S >= 1 (any S; partial tiles are masked), D in {64, 128},
- *     B*H*S*D < 2^40 elements, any finite scale.
+ *     B*H*S*D < 2^40 elements, S*D < 2^29, any finite scale.
+ *   - Every load stays inside the extent of the tensor it reads (a partial
+ *     last tile is zero-filled on chip), so buffers may be allocated to their
+ *     exact size with nothing mapped after them.
  *   - Arithmetic: bf16 inputs, fp32 accumulation in the matrix cores, fp32
  *     softmax statistics, outputs rounded to nearest-even.
  */
