@@ -45,14 +45,14 @@ TRAFFIC_SOURCES = ("exact_attention_128_amd/csrc/attn_bwd.hip",
                    "exact_attention_128_amd/csrc/attn_internal.h",
                    "exact_attention_128_amd/build.py")
 TRAFFIC = {"workload": "bwd_causal_s4k", "read_bytes": 229614928, "write_bytes": 67108864,
-           "sources_sha256": "ffa7a277de202f028ae2abf64cfb34dff70e6be120a95896f664e5361e02f341"}
+           "sources_sha256": "66e0a4429efccac5dbb6ea76b8eacd3bc9f34ee3f7fdb1a7643a40a8e531a731"}
 # the same for the forward on the causal S=8192 workload
 # (profiles/fwd_causal_s8k_counters.md)
 FWD_TRAFFIC_SOURCES = ("exact_attention_128_amd/csrc/attn_fwd.hip",
                        "exact_attention_128_amd/csrc/gfx950.h",
                        "exact_attention_128_amd/csrc/attn_internal.h")
 FWD_TRAFFIC = {"workload": "fwd_causal_s8k", "read_bytes": 1344340421, "write_bytes": 136317888,
-               "sources_sha256": "53288e5b7a021b1c7917e82f2caaf2e0ee6e048d2581d9a87da32cdd1530b587"}
+               "sources_sha256": "072ce87ed9b69eea569520518ab0dec9c9016dbff13243495974ac5827f6090e"}
 
 
 def measured_traffic(workload, record=None, sources=None):
@@ -203,6 +203,18 @@ def main():
                           "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
             log("fwd leg %s: %.4f ms  %.1f TFLOPS (%.1f%%)  %.1f GB/s algorithmic HBM" % (
                 name, ms, tf, 100 * tf / PEAK_BF16_TFLOPS, gbs))
+            if lw.causal:
+                # untimed: how often the conditional rescale fires (the counting
+                # forward, attn_fwd_rescale_events), at the default threshold
+                # 2^32 and at FA4's 2^8
+                ev = {}
+                for tau in (32.0, 8.0):
+                    _, _, tests, fired = A.fwd_rescale_events(lq, lk, lv, causal=lw.causal,
+                                                              scale=lw.scale, rescale_log2=tau)
+                    ev["tau%d" % tau] = {"tests": tests, "fired": fired,
+                                         "rate": round(fired / max(1, tests), 4)}
+                legs[name]["rescale_events"] = ev
+                log("  rescale events %s: %s" % (name, ev))
             del lq, lk, lv, lo, ll
             torch.cuda.empty_cache()
         # Context for the MFMA peak on this part: a plain vendor-library bf16 GEMM

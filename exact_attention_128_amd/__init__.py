@@ -18,8 +18,8 @@ import math
 from . import _lib
 from ._lib import AttnError, load, library_path  # noqa: F401
 
-__all__ = ["fwd", "bwd", "fwd_out", "bwd_out", "bwd_workspace_size", "AttnError", "load",
-           "library_path"]
+__all__ = ["fwd", "bwd", "fwd_out", "fwd_rescale_events", "bwd_out", "bwd_workspace_size",
+           "AttnError", "load", "library_path"]
 
 
 def _check(t, name, shape=None):
@@ -77,6 +77,32 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None,
     lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
     fwd_out(q, k, v, o, lse, causal=causal, scale=scale, rescale_log2=rescale_log2)
     return o, lse
+
+
+def fwd_rescale_events(q, k, v, causal: bool = False, scale: float | None = None,
+                       rescale_log2: float = 32.0):
+    """Diagnostic forward (attn_fwd_rescale_events): returns (O, LSE, tests,
+    rescales), the counts of conditional-rescale tests (one per wave of 32
+    query rows and 128-key step after the first) and of those that fired.
+    Synchronises the current stream to read the counters."""
+    import torch
+    _check(q, "q")
+    B, H, S, D = q.shape
+    _check(k, "k", q.shape)
+    _check(v, "v", q.shape)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    ev = torch.zeros(2, dtype=torch.int64, device=q.device)
+    rc = _lib.load().attn_fwd_rescale_events(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                             o.data_ptr(), lse.data_ptr(), B, H, S, D,
+                                             float(scale), int(bool(causal)),
+                                             float(rescale_log2), ev.data_ptr(),
+                                             _stream(q.device))
+    _lib.raise_for(rc, "attn_fwd_rescale_events")
+    tests, rescales = (int(x) for x in ev.cpu().tolist())
+    return o, lse, tests, rescales
 
 
 def bwd_workspace_size(B: int, H: int, S: int, D: int) -> int:

@@ -36,13 +36,16 @@ int hip_status(hipError_t e) {
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-             int S, int D, float scale, int causal, float tau, attn_stream_t stream) {
+             int S, int D, float scale, int causal, float tau, attn_stream_t stream,
+             unsigned long long* events = nullptr, bool counting = false) {
   if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
+  if (counting && !events) return ATTN_ERR_NULL;
   int rc = check_shape(B, H, S, D);
   if (rc) return rc;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
       !aligned(lse, 4))
     return ATTN_ERR_ALIGN;
+  if (counting && !aligned(events, 8)) return ATTN_ERR_ALIGN;
   if (!isfinite(scale)) return ATTN_ERR_SCALE;
   if (!(tau >= 0.0f && tau <= 64.0f)) return ATTN_ERR_SCALE;
 
@@ -63,7 +66,10 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
   if (scale == 0.0f) p.qand = 0u;
   p.c = (scale == 0.0f) ? 1.0f : fabsf(scale) * attn::kLog2eHost;
   p.tau = tau;
-  return hip_status(attn::launch_fwd(p, D, causal != 0, reinterpret_cast<hipStream_t>(stream)));
+  p.events = events;
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  return hip_status(counting ? attn::launch_fwd_counting(p, D, causal != 0, st)
+                             : attn::launch_fwd(p, D, causal != 0, st));
 }
 
 }  // namespace
@@ -79,6 +85,13 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
                 int S, int D, float scale, int causal, float rescale_log2,
                 attn_stream_t stream) {
   return fwd_impl(q, k, v, o, lse, B, H, S, D, scale, causal, rescale_log2, stream);
+}
+
+int attn_fwd_rescale_events(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int B, int H, int S, int D, float scale, int causal,
+                            float rescale_log2, unsigned long long* events,
+                            attn_stream_t stream) {
+  return fwd_impl(q, k, v, o, lse, B, H, S, D, scale, causal, rescale_log2, stream, events, true);
 }
 
 size_t attn_bwd_workspace_size(int B, int H, int S, int D) {

@@ -85,7 +85,10 @@ struct FwdTile {
   static constexpr int VPIECE = 2 * DB * (BC / 16);
 };
 
-template <int D, bool CAUSAL>
+// COUNT: the diagnostic instantiation behind attn_fwd_rescale_events, which
+// also counts the rescale tests and the rescales (same arithmetic, same
+// results; the production kernels are the COUNT = false ones).
+template <int D, bool CAUSAL, bool COUNT = false>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(FwdParams p) {
   using T = FwdTile<D>;
@@ -209,6 +212,7 @@ void attn_fwd_kernel(FwdParams p) {
   for (int i = 0; i < DB; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[i][r] = 0.0f;
+  int n_tests = 0, n_rescales = 0;   // COUNT only; wave-uniform
   float m_run = 0.0f;        // stale row max in log2 units (scores * c); set by step 0
   float l_f = 0.0f;          // sum of fp32 P: normalises O and gives the LSE
   const float c = p.c;
@@ -370,7 +374,9 @@ void attn_fwd_kernel(FwdParams p) {
     __builtin_amdgcn_sched_barrier(0);
     f32x16 e[4];
     float t = expo(s, 0.0f, e);
+    if constexpr (COUNT) ++n_tests;
     if (wave_any(t > thresh)) {
+      if constexpr (COUNT) ++n_rescales;
       const float mx = fmaxf(row_max(s), 0.0f);
       rescale(__builtin_amdgcn_exp2f(-mx));
       m_run += mx;
@@ -473,9 +479,15 @@ void attn_fwd_kernel(FwdParams p) {
       }
     if (h == 0) p.lse[(size_t)bh * S + qrow] = (m_run + __builtin_amdgcn_logf(lf)) * kLn2;
   }
+  if constexpr (COUNT) {
+    if (lane == 0 && n_tests > 0) {
+      atomicAdd(p.events, (unsigned long long)n_tests);
+      atomicAdd(p.events + 1, (unsigned long long)n_rescales);
+    }
+  }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool COUNT = false>
 static hipError_t launch_fwd_t(const FwdParams& p0, hipStream_t stream) {
   constexpr int NW = 8;
   FwdParams p = p0;
@@ -485,13 +497,22 @@ static hipError_t launch_fwd_t(const FwdParams& p0, hipStream_t stream) {
   const long grid = (long)p.bh * p.nqb;
   if (grid <= 0 || grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
   void* args[] = {&p};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_kernel<D, CAUSAL>),
+  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_kernel<D, CAUSAL, COUNT>),
                          dim3((unsigned)grid), dim3(NW * 64), args, 0, stream);
 }
 
 hipError_t launch_fwd(const FwdParams& p, int D, bool causal, hipStream_t stream) {
   if (D == 128) return causal ? launch_fwd_t<128, true>(p, stream) : launch_fwd_t<128, false>(p, stream);
   if (D == 64) return causal ? launch_fwd_t<64, true>(p, stream) : launch_fwd_t<64, false>(p, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_fwd_counting(const FwdParams& p, int D, bool causal, hipStream_t stream) {
+  if (!p.events) return hipErrorInvalidValue;
+  if (D == 128)
+    return causal ? launch_fwd_t<128, true, true>(p, stream) : launch_fwd_t<128, false, true>(p, stream);
+  if (D == 64)
+    return causal ? launch_fwd_t<64, true, true>(p, stream) : launch_fwd_t<64, false, true>(p, stream);
   return hipErrorInvalidValue;
 }
 

@@ -25,6 +25,7 @@ struct FwdParams {
   float tau;      // rescale threshold in log2 units
   float thresh;   // 2^tau: a lane's partial weight sum above it triggers a rescale
   int xcd_heads;  // heads per XCD for the XCD-aware block order, 0 = plain order
+  unsigned long long* events;  // diagnostic counters (see attn_fwd_rescale_events), or null
 };
 
 // One backward launch.
@@ -54,6 +55,7 @@ struct BwdParams {
 };
 
 hipError_t launch_fwd(const FwdParams& p, int D, bool causal, hipStream_t stream);
+hipError_t launch_fwd_counting(const FwdParams& p, int D, bool causal, hipStream_t stream);
 hipError_t launch_bwd(const BwdParams& p, int D, bool causal, unsigned phases, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdParams& p, int D, bool causal, hipStream_t stream);
 

@@ -73,10 +73,11 @@ enum attn_status {
  *   scale    multiplies the logits before masking and softmax (usually 1/sqrt(D)).
  *   causal   nonzero: key j is visible to query i iff j <= i.
  * The online softmax rescales the running output only when a row's maximum
- * grows by more than 32 (log2 units) over the stale maximum it is using, the
- * conditional-rescaling idea of FA4 (Tencent Cloud article, section 7): the
- * unnormalised weights stay below 2^32, far inside the fp32 and bf16 exponent
- * range of the sums and the PV product.  The result is the same for every
+ * grows by about 32 (log2 units) over the stale maximum it is using (the test
+ * is described at attn_fwd_ex), the conditional-rescaling idea of FA4
+ * (Tencent Cloud article, section 7): the unnormalised weights stay below
+ * 2^32, far inside the fp32 and bf16 exponent range of the sums and the PV
+ * product.  The result is the same for every
  * threshold, see attn_fwd_ex.
  * Returns ATTN_OK or an attn_status code; nothing is written on error.
  */
@@ -86,16 +87,39 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 
 /*
  * Forward with an explicit rescale threshold `rescale_log2` in [0, 64]:
- * the running output of a row is rescaled only when the row maximum has grown
- * by more than rescale_log2 (in units of log2) past the maximum in use;
- * 0 rescales whenever the maximum grows.  Every threshold yields the same
- * exact result up to rounding (the stale maximum cancels between numerator
- * and denominator).  Other arguments as attn_fwd.  Out-of-range threshold:
- * ATTN_ERR_SCALE.
+ * a wave of 32 query rows rescales its running outputs after a 128-key step
+ * when some lane's sum of the step's weights, taken against the stale row
+ * maximum, exceeds 2^rescale_log2.  That happens whenever a row maximum has
+ * grown by more than rescale_log2 (in units of log2) past the maximum in
+ * use, and may happen a little earlier (many weights close to the bound);
+ * 0 rescales at every growth and on most steps besides.  Every threshold
+ * yields the same exact result up to rounding (the stale maximum cancels
+ * between numerator and denominator).  Other arguments as attn_fwd.
+ * Out-of-range threshold: ATTN_ERR_SCALE.
  */
 int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
                 int B, int H, int S, int D, float scale, int causal,
                 float rescale_log2, attn_stream_t stream);
+
+/*
+ * Diagnostic forward that also counts the conditional-rescale events (the FA4
+ * technique of rescaling only when the maximum threatens the number range,
+ * Tencent Cloud article, section 7).  The kernel tests once per wave (32
+ * query rows) and 128-key step after the row block's first step; a test fires
+ * when some lane's sum of the step's weights, taken against the stale
+ * maximum, exceeds 2^rescale_log2 — then the wave's maxima move up, O and the
+ * sums are rescaled and the step's weights recomputed.
+ *   events   device pointer to two unsigned 64-bit counters, 8-byte aligned,
+ *            owned by the caller, who zeroes them: the launch ADDS the number
+ *            of tests to events[0] and the number that fired to events[1].
+ * Computes the same O and LSE as attn_fwd_ex with the same arguments, bit for
+ * bit.  Other arguments and errors as attn_fwd_ex; events == NULL:
+ * ATTN_ERR_NULL.
+ */
+int attn_fwd_rescale_events(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int B, int H, int S, int D, float scale, int causal,
+                            float rescale_log2, unsigned long long* events,
+                            attn_stream_t stream);
 
 /*
  * Bytes of device workspace attn_bwd needs for this shape (0 if the shape is

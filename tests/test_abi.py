@@ -59,6 +59,11 @@ def test_fwd_validation(lib):
     assert lib.attn_fwd_ex(P, P, P, P, P, 1, 1, 16, 128, 0.1, 0, -1.0, None) == 6
     assert lib.attn_fwd_ex(P, P, P, P, P, 1, 1, 16, 128, 0.1, 0, 65.0, None) == 6
     assert lib.attn_fwd_ex(P, P, P, P, P, 1, 1, 16, 128, 0.1, 0, float("nan"), None) == 6
+    ev = lib.attn_fwd_rescale_events
+    assert ev(P, P, P, P, P, 1, 1, 16, 128, 0.1, 0, 32.0, None, None) == 1
+    assert ev(P, P, P, P, P, 1, 1, 16, 128, 0.1, 0, 32.0, P + 4, None) == 4
+    assert ev(P, P, P, P, P, 1, 1, 16, 96, 0.1, 0, 32.0, P, None) == 3
+    assert ev(P, P, P, P, P, 1, 1, 16, 128, 0.1, 0, 70.0, P, None) == 6
 
 
 def test_bwd_validation(lib):

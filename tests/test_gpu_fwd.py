@@ -71,6 +71,46 @@ def test_rescale_threshold_gives_same_result():
         assert np.all(diff <= bound), "tau=%g vs 0: max diff %.3e" % (tau, diff.max())
 
 
+def _expected_tests(B, H, S, causal):
+    """Rescale tests the kernel makes: one per wave (32 query rows) and 128-key
+    step after the wave's first step."""
+    n = 0
+    for qw in range(0, S, 32):
+        wend = min(S, qw + 32) if causal else S
+        n += max(0, -(-wend // 128) - 1)
+    return B * H * n
+
+
+@pytest.mark.parametrize("name", ["fwd_stress_s16k", "fwd_causal_s8k", "fwd_s2k"])
+def test_rescale_event_counts(name):
+    """The counting forward gives attn_fwd_ex's outputs bit for bit, makes exactly
+    the number of rescale tests the shape implies, and fires fewer rescales at a
+    higher threshold.  On unit-variance scores no later score exceeds the stale
+    maximum by more than ~8 nats (under 2^12 per weight), so a lane's 64 weights
+    stay far below 2^32 and tau = 32 never fires there."""
+    import torch
+    import exact_attention_128_amd as A
+    w = ai.WORKLOADS[name]
+    bits = ai.workload_inputs(w)
+    dev = torch.device("cuda", 0)
+    q, k, v = (ai.to_torch_bf16(bits[n], dev) for n in ("q", "k", "v"))
+    fired = {}
+    for tau in (0.0, 8.0, 32.0):
+        o, lse, tests, resc = A.fwd_rescale_events(q, k, v, causal=w.causal, scale=w.scale,
+                                                   rescale_log2=tau)
+        o2, lse2 = A.fwd(q, k, v, causal=w.causal, scale=w.scale, rescale_log2=tau)
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int16), o2.view(torch.int16)), "O differs at tau=%g" % tau
+        assert torch.equal(lse, lse2), "LSE differs at tau=%g" % tau
+        assert tests == _expected_tests(w.B, w.H, w.S, w.causal), (tests, tau)
+        fired[tau] = resc
+        print(name, "tau", tau, "tests", tests, "rescales", resc,
+              "(%.2f%%)" % (100.0 * resc / max(1, tests)))
+    assert fired[0.0] >= fired[8.0] >= fired[32.0]
+    if not w.stress:
+        assert fired[32.0] == 0
+
+
 def test_deterministic():
     bits = ai.make_inputs(2, 4, 777, 128, 5)
     _, l1, b1 = P.gpu_fwd(bits, True, 0.1)
