@@ -29,6 +29,16 @@ def test_ragged_lengths(S, D, causal):
     P.assert_grads_ok(err, "S=%d D=%d causal=%s" % (S, D, causal))
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_multi_block_lengths(D, causal):
+    """Several blocks of every kernel (256-row dQ blocks, 128-key dK/dV blocks
+    walked in 64-query steps) with ragged tails, and B*H = 8, which takes the
+    XCD-aware block order."""
+    err, _ = _case(2, 4, 1500, D, causal, seed=2500 + D + int(causal))
+    P.assert_grads_ok(err, "S=1500 D=%d causal=%s" % (D, causal))
+
+
 @pytest.mark.parametrize("scale", [1.0, -0.2, 0.0])
 def test_scale_values(scale):
     """Off-standard scales.  The 5e-2 bound is stated for unit-variance inputs at

@@ -43,6 +43,15 @@ def test_many_heads(causal):
     P.assert_fwd_ok(err, "odd heads")
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_multi_block_lengths(D, causal):
+    """Several 256-row query blocks and 128-key steps with a ragged tail, and
+    B*H = 8, which takes the XCD-aware block order."""
+    err = _full_case(2, 4, 1500, D, causal, seed=1500 + D + int(causal))
+    P.assert_fwd_ok(err, "S=1500 D=%d causal=%s" % (D, causal))
+
+
 @pytest.mark.parametrize("scale", [1.0, -0.09, 0.0, 0.5])
 def test_scale_values(scale):
     for causal in (False, True):
