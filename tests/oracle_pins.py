@@ -101,6 +101,25 @@ def pin_constant_v(orc):
         _close(o, np.broadcast_to(u, o.shape), 1e-12, "constant V causal=%s" % causal)
 
 
+def pin_rows_of_p(orc):
+    """V = identity (S = D, V_j = e_j) makes O_i the probability row P_i itself:
+    each row is nonnegative and sums to 1, P_ij = exp(s_ij - LSE_i) for every
+    visible key, and causal rows put no weight above the diagonal."""
+    rng = np.random.default_rng(14)
+    S = D = 16
+    q, k = _rand(rng, 1, 1, S, D, scale=1.5), _rand(rng, 1, 1, S, D, scale=1.5)
+    v = np.eye(S)[None, None]
+    for causal in (False, True):
+        o, lse = orc.attn_fwd(q, k, v, 0.4, causal)
+        p, lse = o[0, 0], lse[0, 0]
+        assert np.all(p >= 0.0), "negative probability causal=%s" % causal
+        _close(p.sum(axis=1), np.ones(S), 1e-12, "rows of P sum to 1 causal=%s" % causal)
+        s = 0.4 * q[0, 0] @ k[0, 0].T
+        vis = np.tril(np.ones((S, S), dtype=bool)) if causal else np.ones((S, S), dtype=bool)
+        want = np.where(vis, np.exp(s - lse[:, None]), 0.0)
+        _close(p, want, 1e-12, "P_ij = exp(s_ij - LSE_i) causal=%s" % causal)
+
+
 def pin_causal_row0(orc):
     """Causal row 0 sees key 0 only: O_0 = V_0, LSE_0 = scale * q_0 . k_0."""
     rng = np.random.default_rng(12)
@@ -289,7 +308,7 @@ def pin_backward_invariants(orc):
     _close(dk, np.zeros_like(dk), 1e-11, "constant V dK")
 
 
-FORWARD_PINS = [pin_golden_forward, pin_constant_v, pin_causal_row0, pin_zero_q, pin_key_shift,
+FORWARD_PINS = [pin_golden_forward, pin_constant_v, pin_rows_of_p, pin_causal_row0, pin_zero_q, pin_key_shift,
                 pin_permutation, pin_mpmath_bruteforce, pin_torch_sdpa, pin_rows_match_full]
 BACKWARD_PINS = [pin_golden_backward, pin_finite_differences, pin_torch_autograd,
                  pin_causal_tail_autograd, pin_backward_invariants]
