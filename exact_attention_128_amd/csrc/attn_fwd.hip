@@ -60,8 +60,9 @@
 //   K  [D/8 chunk columns][64 keys][16 bytes]
 //   V  [D/32 feature blocks][64 keys][32 features]
 //
-// l, which normalises O and gives the LSE, is the fp32 sum of P; the PV
-// product consumes P rounded to bf16.
+// Two row sums: O is normalised by the sum of the bf16-rounded P that the PV
+// product consumes (so the weights of O sum to one exactly in the products'
+// own rounding), the LSE takes the fp32 sum of P.
 #include "attn_internal.h"
 #include "gfx950.h"
 
@@ -214,7 +215,9 @@ void attn_fwd_kernel(FwdParams p) {
     for (int r = 0; r < 16; ++r) o[i][r] = 0.0f;
   int n_tests = 0, n_rescales = 0;   // COUNT only; wave-uniform
   float m_run = 0.0f;        // stale row max in log2 units (scores * c); set by step 0
-  float l_f = 0.0f;          // sum of fp32 P: normalises O and gives the LSE
+  float l_f = 0.0f;          // sum of the fp32 weights: gives the LSE
+  float l_b = 0.0f;          // sum of the weights rounded to bf16 (what the PV product
+                             // consumes): normalises O
   const float c = p.c;
   const float thresh = p.thresh;   // 2^tau
 
@@ -338,6 +341,7 @@ void attn_fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
     l_f *= alpha;
+    l_b *= alpha;
   };
   // e = 2^(x - mx) for the kept exponents x; returns this lane's partial sum.
   // All exponentials issue first and the sums follow behind a scheduling
@@ -358,6 +362,19 @@ void attn_fwd_kernel(FwdParams p) {
       for (int r = 0; r < 16; ++r)
         if ((r & 7) != 0) t[2 * i + (r >> 3)] += e[i][r];
     return ((t[0] + t[1]) + (t[2] + t[3])) + ((t[4] + t[5]) + (t[6] + t[7]));
+  };
+  // this lane's sum of its packed bf16 weights (exact products by 1.0 in
+  // v_dot2c_f32_bf16, fp32 accumulation), in four chains
+  auto bsum = [&](const uint32_t (&pk)[4][8]) {
+    const bf16x2 one = __builtin_bit_cast(bf16x2, 0x3F803F80u);
+    float t[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        t[i] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[i][j]), one, t[i],
+                                               false);
+    return (t[0] + t[1]) + (t[2] + t[3]);
   };
   // Softmax of a later step against the stale maximum m, with conditional
   // rescaling.  x = s*c - m is kept until the weights e = 2^x have passed the
@@ -384,6 +401,7 @@ void attn_fwd_kernel(FwdParams p) {
     }
     l_f += t;
     pack(e, pk);
+    l_b += bsum(pk);
   };
 
   // ---- prologue: K of steps 0..2 and V of step 0 requested; once K 0, K 1
@@ -414,6 +432,7 @@ void attn_fwd_kernel(FwdParams p) {
       for (int r = 0; r < 16; ++r) s[i][r] = __builtin_fmaf(s[i][r], c, nm);
     l_f = expo(s, 0.0f, e);
     pack(e, pk);
+    l_b = bsum(pk);
   }
 
   // ---- main loop over steps of 128 keys.  K of step j lives in K slot j % 3,
@@ -461,12 +480,15 @@ void attn_fwd_kernel(FwdParams p) {
   }
   if (grp == 0) sync();
 
-  // ---- epilogue: O = O / l (bf16), LSE = ln2 * (m + log2 l).  l is the
-  //      fp32 sum of the weights; the products used them rounded to bf16,
-  //      which moves O by about 2^-9 / sqrt(keys) relative.
+  // ---- epilogue: O = O / l_b (bf16), LSE = ln2 * (m + log2 l_f).  O is
+  //      normalised by the sum of the same bf16-rounded weights its products
+  //      used (a row dominated by one key then gets exactly that key's V,
+  //      up to the output rounding); the LSE takes the fp32 sum, which the
+  //      rounding of the weights would move by up to 2^-9 relative.
   const float lf = halfwave_sum(l_f);
+  const float lb = halfwave_sum(l_b);
   if (qrow < S) {
-    const float inv = 1.0f / lf;
+    const float inv = 1.0f / lb;
     uint16_t* orow = p.o + head + (size_t)qrow * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)

@@ -59,6 +59,13 @@ def test_scale_values(scale):
         P.assert_fwd_ok(err, "scale=%g causal=%s" % (scale, causal))
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_rising_maximum_d64(causal):
+    """The rising-maximum construction at D = 64 (the S = 16384 workload is D = 128)."""
+    err = _full_case(1, 3, 2100, 64, causal, seed=64, stress=True)
+    P.assert_fwd_ok(err, "rising maximum D=64 causal=%s" % causal)
+
+
 def test_rescale_threshold_gives_same_result():
     """Conditional rescaling is exact: every threshold matches the oracle.  Runs with
     different thresholds use different stale maxima, so P is rounded to bf16 at
@@ -137,15 +144,16 @@ def test_non_default_stream():
 
 
 @pytest.mark.parametrize("name", ["fwd_s2k", "fwd_causal_s8k", "fwd_stress_s16k"])
-def test_full_size_workloads_sampled(name):
-    """Full-size workloads in the benchmark's launch configuration, checked on
-    sampled rows (sequence and tile edges plus random rows of several heads)."""
+def test_full_size_workloads(name):
+    """Full-size workloads in the benchmark's launch configuration, every element
+    of O and LSE against the oracle (about 10 s of oracle time each for the two
+    long causal ones)."""
     w = ai.WORKLOADS[name]
     bits = ai.workload_inputs(w)
     o, lse, _ = P.gpu_fwd(bits, w.causal, w.scale)
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
-    rows = P.sample_rows(w.B, w.H, w.S, n_heads=4, n_rows=96, seed=w.seed)
-    err = P.sampled_fwd_errors(o, lse, bits, w.causal, w.scale, rows)
+    o_ref, lse_ref = P.oracle_fwd_full(bits, w.causal, w.scale)
+    err = P.fwd_errors(o, lse, o_ref, lse_ref)
     print(name, err)
     P.assert_fwd_ok(err, name)
 
