@@ -146,20 +146,7 @@ void attn_fwd_kernel(FwdParams p) {
   const size_t head = (size_t)bh * S * D;
   const uint16_t* __restrict__ Qh = p.q + head;
 
-  // ---- Q fragments (B operand of S^T = K Q^T): lane holds row qrow,
-  //      features 16*kk + 8*h .. +7 for step kk.
-  bf16x8 qf[KK];
-  {
-    const bool ok = qrow < S;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (ok) x = *(const u32x4*)(Qh + (size_t)qrow * D + 16 * kk + 8 * h);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = (x[e] ^ p.qxor) & p.qand;
-      qf[kk] = __builtin_bit_cast(bf16x8, x);
-    }
-  }
+  bf16x8 qf[KK];   // Q fragments, loaded in the prologue
 
   // keys [0, kend) matter to this workgroup, in steps of 2*BC; this wave uses
   // steps [0, wsteps)
@@ -404,19 +391,41 @@ void attn_fwd_kernel(FwdParams p) {
     l_b += bsum(pk);
   };
 
-  // ---- prologue: K of steps 0..2 and V of step 0 requested; once K 0, K 1
-  //      and V 0 have landed, step 0's scores and softmax (the row maxima
-  //      start exact).
+  // ---- prologue.  Waves 4..7 request K of step 0 and every wave its Q rows;
+  //      once they have landed (a full wait, so no load the compiler tracks is
+  //      left pending), K of steps 1..2 and V of steps 0..1 are requested and
+  //      stream in behind step 0's scores and softmax (the row maxima start
+  //      exact).  Each wave then waits for its own pieces of K 1 (waves 4..7)
+  //      or V 0 (waves 0..3), and a barrier makes them visible before the
+  //      first reads of K 1.  K 2 and V 1 are waited for before the next
+  //      barrier of their loading waves (below and at the end of the first
+  //      matrix half), ahead of their first reads.
+  if (grp == 1) fetch_k(0);
+  // Q fragments (B operand of S^T = K Q^T): lane holds row qrow, features
+  // 16*kk + 8*h .. +7 for step kk.  Branch-free: a lane past S loads the
+  // last row and its mask zeroes the values, so the eight loads issue back
+  // to back behind the K request.
+  {
+    const bool ok = qrow < S;
+    const uint16_t* qr = Qh + (size_t)(ok ? qrow : S - 1) * D + 8 * h;
+    const uint32_t qm = ok ? p.qand : 0u;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      u32x4 x = *(const u32x4*)(qr + 16 * kk);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = (x[e] ^ p.qxor) & qm;
+      qf[kk] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+  wait_vmcnt<0>();
+  sync();
   if (grp == 1) {
-    fetch_k(0);
     if (nsteps > 1) fetch_k(1);
     if (nsteps > 2) fetch_k(2);
   } else {
     fetch_v(0);
     if (nsteps > 1) fetch_v(1);
   }
-  wait_vmcnt<0>();
-  sync();
 
   uint32_t pk[4][8];
   if (wsteps > 0) {
@@ -443,7 +452,9 @@ void attn_fwd_kernel(FwdParams p) {
   //      every SIMD one wave's matrix half, at raised priority, meets the
   //      other's softmax half.  Global barriers 2j and 2j+1 close the matrix
   //      halves of step j of waves 0..3 and 4..7 (barrier -1 ends the
-  //      prologue, which loads K of steps 0..2 and V of steps 0..1).
+  //      prologue, by which K of step 1 and V of step 0 have landed; its
+  //      loads of K of step 2 and V of step 1 are waited for before barrier
+  //      0, ahead of their first reads after it).
   //      Loads are issued at the top of the softmax half, where the wave has
   //      time to spare, and waited for at the end of its next matrix half:
   //      waves 0..3 request K of step j+3 after barrier 2j (into the slot of
@@ -454,9 +465,20 @@ void attn_fwd_kernel(FwdParams p) {
   //      barrier 2j+3, after which it is first read.  A wave at its last step
   //      still runs the score products of the (unused) next slot, so the
   //      matrix half has a single code path.
+  if (grp == 1) {
+    if (nsteps > 2) wait_vmcnt<KPW>();   // K 1 landed, K 2 may still be in flight
+    else wait_vmcnt<0>();
+  } else {
+    if (nsteps > 1) wait_vmcnt<VPW>();   // V 0 landed, V 1 may still be in flight
+    else wait_vmcnt<0>();
+  }
+  sync();
   bf16x8 kp[LA];
   kpre_read(1, kp);
-  if (grp == 1) sync();
+  if (grp == 1) {
+    wait_vmcnt<0>();   // K 2, read by waves 0..3 after this barrier
+    sync();
+  }
   for (int j = 0; j < nsteps; ++j) {
     f32x16 sn[4];
     if (j < wsteps) {
