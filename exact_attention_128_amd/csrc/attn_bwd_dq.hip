@@ -110,33 +110,38 @@ void attn_bwd_dq_kernel(BwdParams p) {
   //      also go to the workspace ([B*H][nblk][L2 x 64, -Delta x 64]), where
   //      the dK/dV kernel reads them; rows past S inside the last 64-row
   //      block get zeros there.
+  //      The loads are branch-free (a lane past S loads the last row and a
+  //      mask zeroes the values), so they issue back to back in the
+  //      prologue, behind the first tiles' requests.
   bf16x8 qf[KK], df[KK];
   float nl2 = 0.0f, ndl = 0.0f;
-  {
+  auto load_rows = [&]() {
     const bool ok = qrow < S;
-    const uint16_t* Qr = p.q + head + (size_t)qrow * D + 8 * h;
-    const uint16_t* Dr = p.dout + head + (size_t)qrow * D + 8 * h;
-    const uint16_t* Or = p.o + head + (size_t)qrow * D + 8 * h;
+    const size_t row = (size_t)(ok ? qrow : S - 1);
+    const uint16_t* Qr = p.q + head + row * D + 8 * h;
+    const uint16_t* Dr = p.dout + head + row * D + 8 * h;
+    const uint16_t* Or = p.o + head + row * D + 8 * h;
+    const uint32_t qm = ok ? p.qand : 0u;
+    const uint32_t rm = ok ? 0xffffffffu : 0u;
+    const float lse = p.lse[(size_t)bh * S + row];
     float dsum = 0.0f;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u}, ov = {0u, 0u, 0u, 0u};
-      if (ok) {
-        a = *(const u32x4*)(Qr + 16 * kk);
-        b = *(const u32x4*)(Dr + 16 * kk);
-        ov = *(const u32x4*)(Or + 16 * kk);
-      }
+      u32x4 a = *(const u32x4*)(Qr + 16 * kk);
+      u32x4 b = *(const u32x4*)(Dr + 16 * kk);
+      u32x4 ov = *(const u32x4*)(Or + 16 * kk);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
+        b[e] &= rm;
         dsum = __builtin_fmaf(__uint_as_float(b[e] << 16), __uint_as_float(ov[e] << 16), dsum);
         dsum = __builtin_fmaf(__uint_as_float(b[e] & 0xffff0000u),
                               __uint_as_float(ov[e] & 0xffff0000u), dsum);
-        a[e] = (a[e] ^ p.qxor) & p.qand;
+        a[e] = (a[e] ^ p.qxor) & qm;
       }
       qf[kk] = __builtin_bit_cast(bf16x8, a);
       df[kk] = __builtin_bit_cast(bf16x8, b);
     }
-    const float l2 = ok ? p.lse[(size_t)bh * S + qrow] * kLog2e : 0.0f;
+    const float l2 = ok ? lse * kLog2e : 0.0f;
     ndl = -halfwave_sum(dsum);
     nl2 = -l2;
     if (h == 0 && qrow < p.nblk * 64) {
@@ -144,7 +149,7 @@ void attn_bwd_dq_kernel(BwdParams p) {
       st[0] = l2;
       st[64] = ndl;
     }
-  }
+  };
 
   const int kend = CAUSAL ? min(S, q0 + BR) : S;
   const int ntiles = (kend + BC - 1) / BC;
@@ -181,8 +186,7 @@ void attn_bwd_dq_kernel(BwdParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[i][r] = 0.0f;
   f32x16 dinit;  // this lane's -Delta in every register: where dP^T - Delta starts
-#pragma unroll
-  for (int r = 0; r < 16; ++r) dinit[r] = ndl;
+                 // (set in the prologue)
   const float c = p.cq;
 
   // Per-lane LDS offsets within a slot (each fragment adds a constant):
@@ -302,10 +306,14 @@ void attn_bwd_dq_kernel(BwdParams p) {
         pk[b][i] = pack_bf16x2(s[b][2 * i] * dp[b][2 * i], s[b][2 * i + 1] * dp[b][2 * i + 1]);
   };
 
-  // ---- prologue: tiles 0, 1, 2 requested; tile 0's scores and dS.
+  // ---- prologue: tiles 0, 1, 2 requested, then this lane's query row
+  //      (above); tile 0's scores and dS.
   fetch(0, 0);
   if (ntiles > 1) fetch(1, 1);
   if (ntiles > 2) fetch(2, 2);
+  load_rows();
+#pragma unroll
+  for (int r = 0; r < 16; ++r) dinit[r] = ndl;
   // A full vmcnt(0) here, visible to the compiler, also retires the Q/dO row
   // loads: the compiler cannot count the direct-to-LDS loads issued as
   // inline assembly, so after a partial wait it would take some row loads as
