@@ -51,8 +51,8 @@ TRAFFIC = {"workload": "bwd_causal_s4k", "read_bytes": 229614928, "write_bytes":
 FWD_TRAFFIC_SOURCES = ("exact_attention_128_amd/csrc/attn_fwd.hip",
                        "exact_attention_128_amd/csrc/gfx950.h",
                        "exact_attention_128_amd/csrc/attn_internal.h")
-FWD_TRAFFIC = {"workload": "fwd_causal_s8k", "read_bytes": 1345754547, "write_bytes": 136315904,
-               "sources_sha256": "89fc8dc253a2b1c69abd3fe8fb97f04c50a4d9cb9d2990d5bb8b8d2748247940"}
+FWD_TRAFFIC = {"workload": "fwd_causal_s8k", "read_bytes": 1383277078, "write_bytes": 136327957,
+               "sources_sha256": "0e362226999274409113f2846a76f04db26a54173f82e95b4e8da58710f2179c"}
 
 
 def measured_traffic(workload, record=None, sources=None):
