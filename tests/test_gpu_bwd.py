@@ -104,6 +104,73 @@ def test_non_default_stream():
     P.assert_grads_ok(P.grad_errors(got, ref), "side stream")
 
 
+def test_workspace_contents_do_not_matter():
+    """The workspace is filled with NaN bit patterns before the call: every byte
+    the kernels read is written by the same call first."""
+    import torch
+    import exact_attention_128_amd as A
+    B, H, S, D = 1, 3, 333, 128
+    bits = ai.make_inputs(B, H, S, D, 43, with_dout=True)
+    scale = 1.0 / np.sqrt(D)
+    dev = torch.device("cuda", 0)
+    q, k, v, do = (ai.to_torch_bf16(bits[n], dev) for n in ("q", "k", "v", "do"))
+    o, lse = A.fwd(q, k, v, causal=True, scale=scale)
+    ws = torch.full((A.bwd_workspace_size(B, H, S, D),), 0xFF, dtype=torch.uint8, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    A.bwd_out(q, k, v, o, lse, do, dq, dk, dv, ws, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    got = tuple(ai.bf16_bits_to_f64(ai.torch_bf16_to_bits(t)) for t in (dq, dk, dv))
+    ref = P.oracle_bwd_heads(bits, True, scale, range(B * H))
+    ref = tuple(np.stack([ref[hd][i] for hd in range(B * H)]).reshape(B, H, S, D)
+                for i in range(3))
+    P.assert_grads_ok(P.grad_errors(got, ref), "NaN-filled workspace")
+
+
+def test_concurrent_calls_on_two_streams():
+    """Two host threads enqueue a forward + backward each, of different shapes,
+    on two streams at once (the library keeps no state between calls)."""
+    import threading
+    import torch
+    import exact_attention_128_amd as A
+    dev = torch.device("cuda", 0)
+    cases = [(2, 2, 700, 128, True, 51), (1, 3, 450, 64, False, 52)]
+    inputs, results = [], [None, None]
+    for (B, H, S, D, causal, seed) in cases:
+        bits = ai.make_inputs(B, H, S, D, seed, with_dout=True)
+        inputs.append((bits, tuple(ai.to_torch_bf16(bits[n], dev) for n in ("q", "k", "v", "do"))))
+    torch.cuda.synchronize()
+
+    def work(i):
+        B, H, S, D, causal, seed = cases[i]
+        q, k, v, do = inputs[i][1]
+        st = torch.cuda.Stream()
+        with torch.cuda.stream(st):
+            for _ in range(3):
+                o, lse = A.fwd(q, k, v, causal=causal)
+                grads = A.bwd(q, k, v, o, lse, do, causal=causal)
+        st.synchronize()
+        results[i] = (o, lse, grads)
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    for i, (B, H, S, D, causal, seed) in enumerate(cases):
+        bits = inputs[i][0]
+        scale = 1.0 / np.sqrt(D)
+        o, lse, grads = results[i]
+        o_ref, lse_ref = P.oracle_fwd_full(bits, causal, scale)
+        P.assert_fwd_ok(P.fwd_errors(ai.bf16_bits_to_f64(ai.torch_bf16_to_bits(o)),
+                                     lse.cpu().numpy().astype(np.float64), o_ref, lse_ref),
+                        "thread %d forward" % i)
+        got = tuple(ai.bf16_bits_to_f64(ai.torch_bf16_to_bits(t)) for t in grads)
+        ref = P.oracle_bwd_heads(bits, causal, scale, range(B * H))
+        ref = tuple(np.stack([ref[hd][j] for hd in range(B * H)]).reshape(B, H, S, D)
+                    for j in range(3))
+        P.assert_grads_ok(P.grad_errors(got, ref), "thread %d backward" % i)
+
+
 def test_phase_subsets():
     """attn_bwd_phases: DQ writes the row statistics itself, so DQ then MAIN
     (on a workspace filled with garbage) reproduces the whole backward bit for
