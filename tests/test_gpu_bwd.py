@@ -6,6 +6,7 @@ import numpy as np
 import pytest
 
 import attn_inputs as ai
+import oracle
 import parity as P
 
 pytestmark = pytest.mark.gpu
@@ -102,6 +103,30 @@ def test_non_default_stream():
     ref = tuple(np.stack([ref[hd][i] for hd in range(B * H)]).reshape(B, H, S, D)
                 for i in range(3))
     P.assert_grads_ok(P.grad_errors(got, ref), "side stream")
+
+
+def test_grid_beyond_16_bits():
+    """66 001 heads (B*H not a multiple of 8: plain block order), S = 40, D = 64:
+    every kernel's grid exceeds 65 535 workgroups.  Forward and backward,
+    every element against the oracle."""
+    import torch
+    import exact_attention_128_amd as A
+    B, H, S, D = 1, 66001, 40, 64
+    bits = ai.make_inputs_chunked(B, H, S, D, 61, with_dout=True)
+    scale = 1.0 / np.sqrt(D)
+    dev = torch.device("cuda", 0)
+    q, k, v, do = (ai.to_torch_bf16(bits[n], dev) for n in ("q", "k", "v", "do"))
+    o, lse = A.fwd(q, k, v, causal=True, scale=scale)
+    dq, dk, dv = A.bwd(q, k, v, o, lse, do, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    f64 = {n: ai.bf16_bits_to_f64(bits[n]) for n in bits}
+    o_ref, lse_ref = oracle.attn_fwd(f64["q"], f64["k"], f64["v"], scale, True)
+    P.assert_fwd_ok(P.fwd_errors(ai.bf16_bits_to_f64(ai.torch_bf16_to_bits(o)),
+                                 lse.cpu().numpy().astype(np.float64), o_ref, lse_ref),
+                    "66001 heads forward")
+    ref = oracle.attn_bwd(f64["q"], f64["k"], f64["v"], f64["do"], scale, True)
+    got = tuple(ai.bf16_bits_to_f64(ai.torch_bf16_to_bits(t)) for t in (dq, dk, dv))
+    P.assert_grads_ok(P.grad_errors(got, ref), "66001 heads backward")
 
 
 def test_workspace_contents_do_not_matter():
