@@ -289,6 +289,26 @@ def pin_causal_tail_autograd(orc):
         _close(dv, tv.grad.numpy()[S - n:], 1e-11, "tail dV n=%d" % n)
 
 
+def pin_batched_backward_autograd(orc):
+    """The [B,H,S,D] backward (every head of a batch) against PyTorch CPU fp64
+    autograd of scaled_dot_product_attention over the same 4-D tensors, causal
+    and not.  Each head draws its own values, so a wrong head offset, a head
+    skipped, or a causal flag not passed on to the heads shows up."""
+    import torch
+    rng = np.random.default_rng(23)
+    B, H, S, D, scale = 2, 3, 13, 8, 0.45
+    q, k, v, do = (_rand(rng, B, H, S, D) for _ in range(4))
+    for causal in (False, True):
+        tq, tk, tv = (torch.from_numpy(x.copy()).requires_grad_(True) for x in (q, k, v))
+        out = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal,
+                                                               scale=scale)
+        out.backward(torch.from_numpy(do))
+        dq, dk, dv = orc.attn_bwd(q, k, v, do, scale, causal)
+        _close(dq, tq.grad.numpy(), 1e-11, "batched dQ causal=%s" % causal)
+        _close(dk, tk.grad.numpy(), 1e-11, "batched dK causal=%s" % causal)
+        _close(dv, tv.grad.numpy(), 1e-11, "batched dV causal=%s" % causal)
+
+
 def pin_backward_invariants(orc):
     rng = np.random.default_rng(21)
     S, D = 24, 8
@@ -311,5 +331,5 @@ def pin_backward_invariants(orc):
 FORWARD_PINS = [pin_golden_forward, pin_constant_v, pin_rows_of_p, pin_causal_row0, pin_zero_q, pin_key_shift,
                 pin_permutation, pin_mpmath_bruteforce, pin_torch_sdpa, pin_rows_match_full]
 BACKWARD_PINS = [pin_golden_backward, pin_finite_differences, pin_torch_autograd,
-                 pin_causal_tail_autograd, pin_backward_invariants]
+                 pin_causal_tail_autograd, pin_batched_backward_autograd, pin_backward_invariants]
 ALL_PINS = FORWARD_PINS + BACKWARD_PINS

@@ -59,6 +59,10 @@ MUTANTS = [
      "for (long r = c + 1; r < n; ++r) {", 1),
     ("tail_p_scale_dropped", "const double p = exp(scale * dot - lse[r]);",
      "const double p = exp(dot - lse[r]);", 0),
+    ("batched_head_offset", "const long off = hd * S * D;", "const long off = hd * S;", 1),
+    ("batched_causal_dropped", "scale, causal, dq + off", "scale, 0, dq + off", 1),
+    ("batched_first_batch_only", "for (long hd = 0; hd < B * H; ++hd) {",
+     "for (long hd = 0; hd < H; ++hd) {", 1),
 ]
 
 
