@@ -22,7 +22,8 @@ __all__ = ["fwd", "bwd", "fwd_out", "fwd_rescale_events", "bwd_out", "bwd_worksp
            "AttnError", "load", "library_path"]
 
 
-def _check(t, name, shape=None):
+def _check(t, name, shape=None, device=None):
+    """bf16, contiguous, 4-D, on a GPU -- and on `device` (q's) when given."""
     import torch
     if not isinstance(t, torch.Tensor):
         raise TypeError("%s must be a torch.Tensor" % name)
@@ -30,12 +31,25 @@ def _check(t, name, shape=None):
         raise TypeError("%s must be torch.bfloat16, got %s" % (name, t.dtype))
     if t.device.type != "cuda":
         raise ValueError("%s must be on a GPU device" % name)
+    if device is not None and t.device != device:
+        raise ValueError("%s is on %s, q on %s" % (name, t.device, device))
     if not t.is_contiguous():
         raise ValueError("%s must be contiguous [B,H,S,D]" % name)
     if t.dim() != 4:
         raise ValueError("%s must be 4-D [B,H,S,D]" % name)
     if shape is not None and tuple(t.shape) != tuple(shape):
         raise ValueError("%s shape %s != %s" % (name, tuple(t.shape), tuple(shape)))
+
+
+def _check_lse(lse, B, H, S, device):
+    """fp32, contiguous [B,H,S], on q's device (the kernels write or read it)."""
+    import torch
+    if not isinstance(lse, torch.Tensor):
+        raise TypeError("lse must be a torch.Tensor")
+    if lse.device != device:
+        raise ValueError("lse is on %s, q on %s" % (lse.device, device))
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, S) or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [B,H,S]")
 
 
 def _stream(device):
@@ -46,14 +60,12 @@ def _stream(device):
 def fwd_out(q, k, v, o, lse, causal: bool = False, scale: float | None = None,
             rescale_log2: float | None = None) -> None:
     """Forward into caller-provided o (bf16 [B,H,S,D]) and lse (fp32 [B,H,S])."""
-    import torch
     _check(q, "q")
     B, H, S, D = q.shape
-    _check(k, "k", q.shape)
-    _check(v, "v", q.shape)
-    _check(o, "o", q.shape)
-    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, S) or not lse.is_contiguous():
-        raise ValueError("lse must be contiguous float32 [B,H,S]")
+    _check(k, "k", q.shape, q.device)
+    _check(v, "v", q.shape, q.device)
+    _check(o, "o", q.shape, q.device)
+    _check_lse(lse, B, H, S, q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     st = _stream(q.device)
@@ -88,8 +100,8 @@ def fwd_rescale_events(q, k, v, causal: bool = False, scale: float | None = None
     import torch
     _check(q, "q")
     B, H, S, D = q.shape
-    _check(k, "k", q.shape)
-    _check(v, "v", q.shape)
+    _check(k, "k", q.shape, q.device)
+    _check(v, "v", q.shape, q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     o = torch.empty_like(q)
@@ -117,13 +129,11 @@ def bwd_out(q, k, v, o, lse, do, dq, dk, dv, workspace, causal: bool = False,
     """Backward into caller-provided dq, dk, dv and a uint8 workspace tensor.
 
     `phases` selects a subset of the three launches (see attn_bwd_phases)."""
-    import torch
     _check(q, "q")
     B, H, S, D = q.shape
     for name, t in (("k", k), ("v", v), ("o", o), ("do", do), ("dq", dq), ("dk", dk), ("dv", dv)):
-        _check(t, name, q.shape)
-    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, S) or not lse.is_contiguous():
-        raise ValueError("lse must be contiguous float32 [B,H,S]")
+        _check(t, name, q.shape, q.device)
+    _check_lse(lse, B, H, S, q.device)
     if workspace.device != q.device or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous tensor on q's device")
     if scale is None:

@@ -13,6 +13,11 @@ namespace {
 thread_local int g_last_hip_error = 0;
 
 constexpr int64_t kMaxElems = int64_t(1) << 40;
+// 256-row query blocks per launch: the forward and dQ kernels run one
+// 512-thread workgroup per block on a 1-D grid, whose work-item count must
+// stay below 2^32; the dK/dV kernel's 256-thread workgroups per 128-key block
+// then stay below it too (ceil(S/128) <= 2 ceil(S/256)).
+constexpr int64_t kMaxRowBlocks = int64_t(1) << 23;
 
 int check_shape(int B, int H, int S, int D) {
   if (B < 1 || H < 1 || S < 1) return ATTN_ERR_SHAPE;
@@ -22,8 +27,13 @@ int check_shape(int B, int H, int S, int D) {
   if (bh * S * D >= kMaxElems) return ATTN_ERR_SHAPE;
   // the kernels address one head's [S][D] bf16 slab with 32-bit byte offsets
   if (int64_t(S) * D >= (int64_t(1) << 29)) return ATTN_ERR_SHAPE;
+  if (bh * ((int64_t(S) + 255) / 256) >= kMaxRowBlocks) return ATTN_ERR_SHAPE;
   return ATTN_OK;
 }
+
+// The kernels multiply each fp32 score by |scale| * log2(e); a scale whose
+// product with log2(e) overflows fp32 would turn every weight into NaN.
+bool scale_ok(float scale) { return isfinite(scale) && isfinite(fabsf(scale) * attn::kLog2eHost); }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -46,7 +56,7 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
       !aligned(lse, 4))
     return ATTN_ERR_ALIGN;
   if (counting && !aligned(events, 8)) return ATTN_ERR_ALIGN;
-  if (!isfinite(scale)) return ATTN_ERR_SCALE;
+  if (!scale_ok(scale)) return ATTN_ERR_SCALE;
   if (!(tau >= 0.0f && tau <= 64.0f)) return ATTN_ERR_SCALE;
 
   attn::FwdParams p{};
@@ -113,7 +123,7 @@ int attn_bwd_phases(const void* q, const void* k, const void* v, const void* o,
       !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
       !aligned(lse, 4) || !aligned(workspace, 256))
     return ATTN_ERR_ALIGN;
-  if (!isfinite(scale)) return ATTN_ERR_SCALE;
+  if (!scale_ok(scale)) return ATTN_ERR_SCALE;
   if (workspace_bytes < attn_bwd_workspace_size(B, H, S, D)) return ATTN_ERR_WORKSPACE;
 
   attn::BwdParams p{};
@@ -153,12 +163,14 @@ const char* attn_strerror(int status) {
   switch (status) {
     case ATTN_OK: return "success";
     case ATTN_ERR_NULL: return "a required pointer is NULL";
-    case ATTN_ERR_SHAPE: return "invalid shape: B, H and S must be >= 1 and B*H*S*D < 2^40";
+    case ATTN_ERR_SHAPE:
+      return "invalid shape: B, H, S >= 1, B*H*S*D < 2^40, S*D < 2^29, B*H*ceil(S/256) < 2^23";
     case ATTN_ERR_HEAD_DIM: return "unsupported head dimension: D must be 64 or 128";
     case ATTN_ERR_ALIGN:
       return "misaligned pointer: bf16 tensors need 16 bytes, LSE 4, workspace 256";
     case ATTN_ERR_WORKSPACE: return "workspace smaller than attn_bwd_workspace_size()";
-    case ATTN_ERR_SCALE: return "scale not finite, or rescale threshold outside [0, 64]";
+    case ATTN_ERR_SCALE:
+      return "scale (or scale*log2(e)) not finite, or rescale threshold outside [0, 64]";
     case ATTN_ERR_UNSUPPORTED: return "request not supported by this build";
     case ATTN_ERR_HIP: return "HIP runtime error (see attn_last_hip_error)";
     default: return "unknown status code";

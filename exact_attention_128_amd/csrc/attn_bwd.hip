@@ -30,6 +30,7 @@
 // 16-byte reads of the score products (32 rows of one chunk column per half
 // wave) and the transposing reads of the gradient products (4 rows x 4 chunk
 // columns per half wave).
+#include <algorithm>
 #include <utility>
 
 #include "attn_internal.h"
@@ -73,33 +74,38 @@ struct BwdTile {
 };
 
 // ---------------------------------------------------------------- pre
+// Grid-stride over the padded rows: LPR consecutive lanes share a row, and
+// the stride is a multiple of LPR, so the lanes of one row always run the
+// same iterations (the row's shuffle reduction never reads an idle lane).
 template <int D>
 __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(BwdParams p, long rows_pad) {
   constexpr int LPR = D / 8;  // lanes per row, 8 elements each
-  const long gid = (long)blockIdx.x * 256 + threadIdx.x;
-  const long rp = gid / LPR;  // row over [B*H][nblk * 64]
-  const int c = (int)(gid % LPR);
+  const long stride = (long)gridDim.x * 256;
   const int per = p.nblk * 64;
-  const long bh = rp / per;
-  const int r = (int)(rp % per);
-  const bool valid = rp < rows_pad && r < p.S;
-  const long row = bh * p.S + r;
-  float acc = 0.0f;
-  if (valid) {
-    const u32x4 a = *(const u32x4*)(p.o + row * D + c * 8);
-    const u32x4 b = *(const u32x4*)(p.dout + row * D + c * 8);
+  for (long gid = (long)blockIdx.x * 256 + threadIdx.x; gid < rows_pad * LPR; gid += stride) {
+    const long rp = gid / LPR;  // row over [B*H][nblk * 64]
+    const int c = (int)(gid % LPR);
+    const long bh = rp / per;
+    const int r = (int)(rp % per);
+    const bool valid = r < p.S;
+    const long row = bh * p.S + r;
+    float acc = 0.0f;
+    if (valid) {
+      const u32x4 a = *(const u32x4*)(p.o + row * D + c * 8);
+      const u32x4 b = *(const u32x4*)(p.dout + row * D + c * 8);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc = __builtin_fmaf(bf16_lo(a[e]), bf16_lo(b[e]), acc);
-      acc = __builtin_fmaf(bf16_hi(a[e]), bf16_hi(b[e]), acc);
+      for (int e = 0; e < 4; ++e) {
+        acc = __builtin_fmaf(bf16_lo(a[e]), bf16_lo(b[e]), acc);
+        acc = __builtin_fmaf(bf16_hi(a[e]), bf16_hi(b[e]), acc);
+      }
     }
-  }
 #pragma unroll
-  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  if (rp < rows_pad && c == 0) {
-    float* st = p.stats + bh * (long)per * 2 + (r / 64) * 128 + (r % 64);
-    st[0] = valid ? p.lse[row] * kLog2e : 0.0f;
-    st[64] = valid ? -acc : 0.0f;
+    for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    if (c == 0) {
+      float* st = p.stats + bh * (long)per * 2 + (r / 64) * 128 + (r % 64);
+      st[0] = valid ? p.lse[row] * kLog2e : 0.0f;
+      st[64] = valid ? -acc : 0.0f;
+    }
   }
 }
 
@@ -440,7 +446,9 @@ static hipError_t launch_bwd_t(const BwdParams& p0, unsigned phases, hipStream_t
   if ((phases & 1u) && !(phases & 4u)) {
     const long rows_pad = (long)p.bh * p.nblk * 64;
     const long threads = rows_pad * (D / 8);
-    const long grid = (threads + 255) / 256;
+    // at most 1024 workgroups (four per CU), grid-stride beyond: this
+    // bandwidth-bound kernel needs no more to fill the chip
+    const long grid = std::min((threads + 255) / 256, 1024L);
     void* args[] = {&p, (void*)&rows_pad};
     e = hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_pre_kernel<D>),
                         dim3((unsigned)grid), dim3(256), args, 0, stream);
@@ -453,7 +461,7 @@ static hipError_t launch_bwd_t(const BwdParams& p0, unsigned phases, hipStream_t
   if (phases & 2u) {
     const long nkb = (p.S + BwdTile<D>::BK - 1) / BwdTile<D>::BK;
     const long grid = nkb * p.bh;
-    if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
+    if (grid * 256 > 0xffffffffL) return hipErrorInvalidConfiguration;
     void* args[] = {&p};
     e = hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_main_kernel<D, CAUSAL>),
                         dim3((unsigned)grid), dim3(256), args, 0, stream);

@@ -382,7 +382,7 @@ static hipError_t launch_dq_t(const BwdParams& p0, hipStream_t stream) {
   BwdParams p = p0;
   p.nqb = (p.S + 32 * NW - 1) / (32 * NW);
   const long grid = (long)p.bh * p.nqb;
-  if (grid <= 0 || grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  if (grid <= 0 || grid * NW * 64 > 0xffffffffL) return hipErrorInvalidConfiguration;
   void* args[] = {&p};
   return hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_dq_kernel<D, CAUSAL>),
                          dim3((unsigned)grid), dim3(NW * 64), args, 0, stream);

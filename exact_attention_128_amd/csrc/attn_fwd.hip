@@ -539,7 +539,7 @@ static hipError_t launch_fwd_t(const FwdParams& p0, hipStream_t stream) {
   p.xcd_heads = (p.bh % 8 == 0) ? p.bh / 8 : 0;
   p.thresh = exp2f(p.tau);
   const long grid = (long)p.bh * p.nqb;
-  if (grid <= 0 || grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  if (grid <= 0 || grid * NW * 64 > 0xffffffffL) return hipErrorInvalidConfiguration;
   void* args[] = {&p};
   return hipLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_kernel<D, CAUSAL, COUNT>),
                          dim3((unsigned)grid), dim3(NW * 64), args, 0, stream);

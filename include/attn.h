@@ -30,7 +30,17 @@
  *   - Arguments are validated on the host before any HIP call.  No C++
  *     exception crosses this boundary.  Calls are thread-safe and re-entrant.
  *   - Supported: B, H, S >= 1 (any S; partial tiles are masked), D in {64, 128},
- *     B*H*S*D < 2^40 elements, S*D < 2^29, any finite scale.
+ *     B*H*S*D < 2^40 elements, S*D < 2^29, and B*H*ceil(S/256) < 2^23 (the
+ *     kernels run one workgroup per 256-row block on a one-dimensional grid,
+ *     whose work-item count must stay below 2^32).
+ *   - Scale: any finite scale whose product with log2(e) is finite (|scale| <
+ *     about 2.36e38; others return ATTN_ERR_SCALE).  The kernels form each
+ *     score as an fp32 dot product multiplied by |scale| * log2(e), so the
+ *     inputs must also keep |scale * q_i . k_j| * log2(e) below FLT_MAX
+ *     (about 3.4e38) for every visible pair: a score past that overflows to
+ *     infinity and the rows it touches come out NaN.  That is the only
+ *     data-dependent limit; unit-variance inputs sit some 35 orders of
+ *     magnitude inside it.
  *   - Every load stays inside the extent of the tensor it reads (a partial
  *     last tile is zero-filled on chip), so buffers may be allocated to their
  *     exact size with nothing mapped after them.
@@ -53,12 +63,14 @@ typedef struct ihipStream_t* attn_stream_t;
 enum attn_status {
   ATTN_OK = 0,
   ATTN_ERR_NULL = 1,        /* a required pointer is NULL                         */
-  ATTN_ERR_SHAPE = 2,       /* B, H or S < 1, B*H*S*D >= 2^40, or S*D >= 2^29     */
+  ATTN_ERR_SHAPE = 2,       /* B, H or S < 1, B*H*S*D >= 2^40, S*D >= 2^29, or
+                               B*H*ceil(S/256) >= 2^23                           */
   ATTN_ERR_HEAD_DIM = 3,    /* D is not 64 or 128                                 */
   ATTN_ERR_ALIGN = 4,       /* a bf16 tensor not 16-byte aligned, LSE not 4-byte,
                                or the workspace not 256-byte aligned              */
   ATTN_ERR_WORKSPACE = 5,   /* workspace smaller than attn_bwd_workspace_size()   */
-  ATTN_ERR_SCALE = 6,       /* scale (or a rescale threshold) not finite / in range */
+  ATTN_ERR_SCALE = 6,       /* scale or scale*log2(e) not finite, or a rescale
+                               threshold out of range                            */
   ATTN_ERR_UNSUPPORTED = 7, /* a valid request this build does not implement      */
   ATTN_ERR_HIP = 8          /* the HIP runtime refused the launch; see
                                attn_last_hip_error()                              */
@@ -125,7 +137,11 @@ int attn_fwd_rescale_events(const void* q, const void* k, const void* v, void* o
  * Bytes of device workspace attn_bwd needs for this shape (0 if the shape is
  * invalid): two fp32 row statistics per query row, LSE_i * log2(e) and
  * -Delta_i = -sum_d dO_id * O_id, stored per 64-row block ([B][H][ceil(S/64)]
- * [2][64]), rounded up to 256 bytes.
+ * [2][64]), rounded up to 256 bytes.  A convention of this library, not of
+ * the pages, which describe no interface: the caller owns every buffer, so
+ * the backward's scratch space is passed in.  (The statistics themselves are
+ * the backward's row sums Delta_i and the recomputation from LSE that the
+ * definition above implies.)
  */
 size_t attn_bwd_workspace_size(int B, int H, int S, int D);
 
@@ -170,6 +186,9 @@ int attn_bwd_phases(const void* q, const void* k, const void* v, const void* o,
                     void* workspace, size_t workspace_bytes, int B, int H, int S,
                     int D, float scale, int causal, unsigned phases,
                     attn_stream_t stream);
+
+/* Error reporting and versioning are conventions of this library (the pages
+ * describe no interface): status codes instead of exceptions across the ABI. */
 
 /* Static English description of a status code (never NULL). */
 const char* attn_strerror(int status);

@@ -106,3 +106,87 @@ def test_python_binding_rejects_cpu_tensors():
         A.fwd(q, q, q)
     with pytest.raises(TypeError):
         A.fwd(q.float(), q, q)
+
+
+def test_grid_limit_boundary(lib):
+    """B*H*ceil(S/256) must stay below 2^23 (one-dimensional grids of 512-thread
+    workgroups).  Just below the limit the shape passes and the next check (a
+    misaligned pointer) answers; at the limit the shape is rejected."""
+    assert _fwd(lib, B=1, H=(1 << 23) - 1, S=1, D=64, v=P + 8) == 4
+    assert _fwd(lib, B=1, H=1 << 23, S=1, D=64, v=P + 8) == 2
+    assert _fwd(lib, B=2, H=1 << 22, S=256, D=64) == 2
+    assert _fwd(lib, B=1, H=1 << 15, S=1 << 16, D=64) == 2
+    assert _fwd(lib, B=1, H=(1 << 15) - 1, S=1 << 16, D=64, v=P + 8) == 4
+    assert lib.attn_bwd_workspace_size(1, 1 << 23, 1, 64) == 0
+    assert lib.attn_bwd_workspace_size(1, (1 << 23) - 1, 1, 64) > 0
+
+
+def test_scale_whose_log2e_multiple_overflows_is_rejected(lib):
+    """|scale| * log2(e) must be finite: the kernels multiply every score by it."""
+    for s in (3.0e38, -3.0e38, 2.4e38):
+        assert _fwd(lib, scale=s) == 6
+        ws = lib.attn_bwd_workspace_size(1, 1, 16, 128)
+        assert lib.attn_bwd(P, P, P, P, P, P, P, P, P, P, ws, 1, 1, 16, 128, s, 1, None) == 6
+
+
+_LAUNCH_PROBE = r"""
+import exact_attention_128_amd as A
+lib = A.load()
+P = 0x10000
+print(lib.attn_fwd(P, P, P, P, P, 1, 1, 16, 128, 0.1, 0, None), lib.attn_last_hip_error())
+ws = lib.attn_bwd_workspace_size(1, 1, 16, 128)
+print(lib.attn_bwd(P, P, P, P, P, P, P, P, P, P, ws, 1, 1, 16, 128, 0.1, 1, None),
+      lib.attn_last_hip_error())
+"""
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="a GPU driver is present: this test "
+                    "only runs where no device can be reached")
+def test_launch_failure_reports_hip_error():
+    """A valid request whose launch the HIP runtime refuses returns ATTN_ERR_HIP,
+    and attn_last_hip_error() gives the runtime's code.  Forced from the host:
+    the probe runs in a child process with every device hidden, on a machine
+    without a GPU driver, so no kernel can start (the pointers are fake)."""
+    import subprocess
+    import sys
+    env = dict(os.environ, HIP_VISIBLE_DEVICES="-1", ROCR_VISIBLE_DEVICES="-1")
+    r = subprocess.run([sys.executable, "-c", _LAUNCH_PROBE], cwd=ROOT, env=env,
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr
+    lines = [l.split() for l in r.stdout.strip().splitlines()]
+    assert len(lines) == 2
+    for rc, hip in lines:
+        assert int(rc) == 8, r.stdout          # ATTN_ERR_HIP
+        assert int(hip) != 0, r.stdout         # the runtime's error code
+
+
+def _fake_cuda(*shape, dtype=None, device="cuda:0"):
+    import torch
+    return torch.empty(*shape, dtype=dtype or torch.bfloat16, device=device)
+
+
+def test_python_binding_rejects_tensors_on_other_devices():
+    """lse and every other tensor must sit on q's device: a host lse would hand
+    the kernels a host pointer.  Checked with fake GPU tensors (no device is
+    touched; a request that got past the checks would reach the C ABI with null
+    pointers and fail there with AttnError, not ValueError)."""
+    import torch
+    from torch._subclasses.fake_tensor import FakeTensorMode
+    import exact_attention_128_amd as A
+    with FakeTensorMode():
+        q = _fake_cuda(1, 1, 8, 64)
+        k, v, o, do = (_fake_cuda(1, 1, 8, 64) for _ in range(4))
+        dq, dk, dv = (_fake_cuda(1, 1, 8, 64) for _ in range(3))
+        lse_host = torch.empty(1, 1, 8, dtype=torch.float32, device="cpu")
+        k_other = _fake_cuda(1, 1, 8, 64, device="cuda:1")
+        ws = torch.empty(512, dtype=torch.uint8, device="cuda:0")
+    with pytest.raises(ValueError, match="lse"):
+        A.fwd_out(q, k, v, o, lse_host)
+    with pytest.raises(ValueError, match="lse"):
+        A.bwd_out(q, k, v, o, lse_host, do, dq, dk, dv, ws)
+    with FakeTensorMode():
+        lse = _fake_cuda(1, 1, 8, dtype=torch.float32)
+    with pytest.raises(ValueError, match="k is on"):
+        A.fwd_out(q, k_other, v, o, lse)
+    with pytest.raises(ValueError, match="k is on"):
+        A.bwd_out(q, k_other, v, o, lse, do, dq, dk, dv, ws)

@@ -196,14 +196,17 @@ def test_concurrent_calls_on_two_streams():
         P.assert_grads_ok(P.grad_errors(got, ref), "thread %d backward" % i)
 
 
-def test_phase_subsets():
+@pytest.mark.parametrize("shape", [(1, 3, 300, 128), (1, 40, 512, 128)])
+def test_phase_subsets(shape):
     """attn_bwd_phases: DQ writes the row statistics itself, so DQ then MAIN
     (on a workspace filled with garbage) reproduces the whole backward bit for
     bit; PRE then MAIN gives the same dK, dV up to the summation order of
-    Delta, both against the oracle."""
+    Delta, both against the oracle.  The second shape has more padded rows
+    than the statistics kernel's grid has lanes (327 680 lanes' worth against
+    1024 x 256), so its grid-stride loop runs twice."""
     import torch
     import exact_attention_128_amd as A
-    B, H, S, D = 1, 3, 300, 128
+    B, H, S, D = shape
     bits = ai.make_inputs(B, H, S, D, 43, with_dout=True)
     scale = 1.0 / np.sqrt(D)
     dev = torch.device("cuda", 0)
