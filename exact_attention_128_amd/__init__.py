@@ -19,7 +19,7 @@ from . import _lib
 from ._lib import AttnError, load, library_path  # noqa: F401
 
 __all__ = ["fwd", "bwd", "fwd_out", "fwd_rescale_events", "bwd_out", "bwd_workspace_size",
-           "AttnError", "load", "library_path"]
+           "bwd_noalloc_out", "AttnError", "load", "library_path"]
 
 
 def _check(t, name, shape=None, device=None):
@@ -145,6 +145,25 @@ def bwd_out(q, k, v, o, lse, do, dq, dk, dv, workspace, causal: bool = False,
                                      B, H, S, D, float(scale), int(bool(causal)), int(phases),
                                      _stream(q.device))
     _lib.raise_for(rc, "attn_bwd")
+
+
+def bwd_noalloc_out(q, k, v, o, lse, do, dq, dk, dv, causal: bool = False,
+                    scale: float | None = None) -> None:
+    """Backward into caller-provided dq, dk, dv with no workspace argument
+    (attn_bwd_noalloc: the library's static per-GPU scratch array).  Calls
+    that overlap on one GPU race on that array."""
+    _check(q, "q")
+    B, H, S, D = q.shape
+    for name, t in (("k", k), ("v", v), ("o", o), ("do", do), ("dq", dq), ("dk", dk), ("dv", dv)):
+        _check(t, name, q.shape, q.device)
+    _check_lse(lse, B, H, S, q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    rc = _lib.load().attn_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                      lse.data_ptr(), do.data_ptr(), dq.data_ptr(),
+                                      dk.data_ptr(), dv.data_ptr(), B, H, S, D, float(scale),
+                                      int(bool(causal)), _stream(q.device))
+    _lib.raise_for(rc, "attn_bwd_noalloc")
 
 
 def bwd(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None):

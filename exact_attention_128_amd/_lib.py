@@ -25,6 +25,9 @@ SIGNATURES = {
                       _i, _vp]),
     "attn_bwd_phases": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _i, _i, _i, _i,
                              _f, _i, ctypes.c_uint, _vp]),
+    "attn_bwd_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f,
+                              _i, _vp]),
+    "attn_noalloc_scratch_bytes": (_sz, []),
     "attn_strerror": (ctypes.c_char_p, [_i]),
     "attn_last_hip_error": (_i, []),
     "attn_version": (_i, []),
@@ -32,7 +35,7 @@ SIGNATURES = {
 
 STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_HEAD_DIM",
           4: "ATTN_ERR_ALIGN", 5: "ATTN_ERR_WORKSPACE", 6: "ATTN_ERR_SCALE",
-          7: "ATTN_ERR_UNSUPPORTED", 8: "ATTN_ERR_HIP"}
+          7: "ATTN_ERR_UNSUPPORTED", 8: "ATTN_ERR_HIP", 9: "ATTN_ERR_SCRATCH"}
 
 
 class AttnError(RuntimeError):

@@ -8,9 +8,23 @@
 #include "../../include/attn.h"
 #include "attn_internal.h"
 
+namespace attn {
+
+namespace {
+thread_local int g_last_hip_error = 0;
+}
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return ATTN_OK;
+  g_last_hip_error = static_cast<int>(e);
+  return ATTN_ERR_HIP;
+}
+
+}  // namespace attn
+
 namespace {
 
-thread_local int g_last_hip_error = 0;
+using attn::hip_status;
 
 constexpr int64_t kMaxElems = int64_t(1) << 40;
 // 256-row query blocks per launch: the forward and dQ kernels run one
@@ -36,12 +50,6 @@ int check_shape(int B, int H, int S, int D) {
 bool scale_ok(float scale) { return isfinite(scale) && isfinite(fabsf(scale) * attn::kLog2eHost); }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
-
-int hip_status(hipError_t e) {
-  if (e == hipSuccess) return ATTN_OK;
-  g_last_hip_error = static_cast<int>(e);
-  return ATTN_ERR_HIP;
-}
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -84,6 +92,26 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
 
 }  // namespace
 
+namespace attn {
+
+// The backward's argument checks other than the workspace's (null pointers,
+// shape, alignment, scale), host-only.
+int check_bwd_args(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dout, const void* dq, const void* dk, const void* dv, int B,
+                   int H, int S, int D, float scale) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return ATTN_ERR_NULL;
+  int rc = check_shape(B, H, S, D);
+  if (rc) return rc;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
+      !aligned(lse, 4))
+    return ATTN_ERR_ALIGN;
+  if (!scale_ok(scale)) return ATTN_ERR_SCALE;
+  return ATTN_OK;
+}
+
+}  // namespace attn
+
 extern "C" {
 
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
@@ -115,15 +143,10 @@ int attn_bwd_phases(const void* q, const void* k, const void* v, const void* o,
                     const float* lse, const void* dout, void* dq, void* dk, void* dv,
                     void* workspace, size_t workspace_bytes, int B, int H, int S, int D,
                     float scale, int causal, unsigned phases, attn_stream_t stream) {
-  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !workspace)
-    return ATTN_ERR_NULL;
-  int rc = check_shape(B, H, S, D);
+  int rc = attn::check_bwd_args(q, k, v, o, lse, dout, dq, dk, dv, B, H, S, D, scale);
   if (rc) return rc;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
-      !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
-      !aligned(lse, 4) || !aligned(workspace, 256))
-    return ATTN_ERR_ALIGN;
-  if (!scale_ok(scale)) return ATTN_ERR_SCALE;
+  if (!workspace) return ATTN_ERR_NULL;
+  if (!aligned(workspace, 256)) return ATTN_ERR_ALIGN;
   if (workspace_bytes < attn_bwd_workspace_size(B, H, S, D)) return ATTN_ERR_WORKSPACE;
 
   attn::BwdParams p{};
@@ -173,11 +196,15 @@ const char* attn_strerror(int status) {
       return "scale (or scale*log2(e)) not finite, or rescale threshold outside [0, 64]";
     case ATTN_ERR_UNSUPPORTED: return "request not supported by this build";
     case ATTN_ERR_HIP: return "HIP runtime error (see attn_last_hip_error)";
+    case ATTN_ERR_SCRATCH:
+      return "problem needs more scratch than the library's static buffer holds "
+             "(attn_bwd_noalloc: attn_bwd_workspace_size() must not exceed "
+             "attn_noalloc_scratch_bytes())";
     default: return "unknown status code";
   }
 }
 
-int attn_last_hip_error(void) { return g_last_hip_error; }
+int attn_last_hip_error(void) { return attn::g_last_hip_error; }
 
 int attn_version(void) { return 100; }
 

@@ -54,6 +54,16 @@ struct BwdParams {
   int xcd_heads;  // heads per XCD for the XCD-aware block order, 0 = plain order
 };
 
+// ATTN_OK for hipSuccess; otherwise records e as the calling thread's last HIP
+// error (attn_last_hip_error) and returns ATTN_ERR_HIP.
+int hip_status(hipError_t e);
+
+// The backward's argument checks other than the workspace's; host only, no
+// HIP call.  Returns ATTN_OK or an attn_status code.
+int check_bwd_args(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dout, const void* dq, const void* dk, const void* dv, int B,
+                   int H, int S, int D, float scale);
+
 hipError_t launch_fwd(const FwdParams& p, int D, bool causal, hipStream_t stream);
 hipError_t launch_fwd_counting(const FwdParams& p, int D, bool causal, hipStream_t stream);
 hipError_t launch_bwd(const BwdParams& p, int D, bool causal, unsigned phases, hipStream_t stream);

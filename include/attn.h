@@ -72,8 +72,10 @@ enum attn_status {
   ATTN_ERR_SCALE = 6,       /* scale or scale*log2(e) not finite, or a rescale
                                threshold out of range                            */
   ATTN_ERR_UNSUPPORTED = 7, /* a valid request this build does not implement      */
-  ATTN_ERR_HIP = 8          /* the HIP runtime refused the launch; see
+  ATTN_ERR_HIP = 8,         /* the HIP runtime refused the launch; see
                                attn_last_hip_error()                              */
+  ATTN_ERR_SCRATCH = 9      /* attn_bwd_noalloc: the shape needs more workspace
+                               than attn_noalloc_scratch_bytes()                  */
 };
 
 /*
@@ -186,6 +188,33 @@ int attn_bwd_phases(const void* q, const void* k, const void* v, const void* o,
                     void* workspace, size_t workspace_bytes, int B, int H, int S,
                     int D, float scale, int causal, unsigned phases,
                     attn_stream_t stream);
+
+/*
+ * Backward that allocates nothing and takes no workspace, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Computes exactly what attn_bwd
+ * computes, with the same kernels, bit for bit; the workspace is a static
+ * device array of attn_noalloc_scratch_bytes() (16 MiB) inside the library,
+ * one per GPU, held until the process ends.  The call makes no hipMalloc,
+ * hipFree or other allocating call (its first call on a device looks up that
+ * device's copy of the array with hipGetSymbolAddress).
+ *   Limit: attn_bwd_workspace_size(B, H, S, D) <= attn_noalloc_scratch_bytes(),
+ *   i.e. B*H*ceil(S/64) <= 32768 (for example B*H = 32 heads up to S = 65536);
+ *   larger shapes return ATTN_ERR_SCRATCH before any HIP call.
+ *   Concurrency: every call on one GPU shares that GPU's array, so calls that
+ *   overlap on one GPU (two streams, or two host threads) race and may return
+ *   wrong gradients; serialise them, or use attn_bwd with a workspace each.
+ *   The array keeps the last call's row statistics; nothing in it needs to
+ *   start at zero.
+ * Arguments (other than the absent workspace) and errors as attn_bwd.
+ */
+int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                     const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                     int B, int H, int S, int D, float scale, int causal,
+                     attn_stream_t stream);
+
+/* Size in bytes of attn_bwd_noalloc's static per-GPU workspace. */
+size_t attn_noalloc_scratch_bytes(void);
 
 /* Error reporting and versioning are conventions of this library (the pages
  * describe no interface): status codes instead of exceptions across the ABI. */

@@ -90,7 +90,7 @@ def test_bwd_validation(lib):
 
 def test_strerror_covers_codes(lib):
     seen = set()
-    for code in range(9):
+    for code in range(10):
         s = lib.attn_strerror(code)
         assert s and s.decode() not in seen
         seen.add(s.decode())
