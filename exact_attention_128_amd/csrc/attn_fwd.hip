@@ -546,6 +546,7 @@ static hipError_t launch_fwd_t(const FwdParams& p0, hipStream_t stream) {
 }
 
 hipError_t launch_fwd(const FwdParams& p, int D, bool causal, hipStream_t stream) {
+  if (p.S <= kShortMaxS) return launch_fwd_short(p, D, causal, stream);
   if (D == 128) return causal ? launch_fwd_t<128, true>(p, stream) : launch_fwd_t<128, false>(p, stream);
   if (D == 64) return causal ? launch_fwd_t<64, true>(p, stream) : launch_fwd_t<64, false>(p, stream);
   return hipErrorInvalidValue;
@@ -553,6 +554,8 @@ hipError_t launch_fwd(const FwdParams& p, int D, bool causal, hipStream_t stream
 
 hipError_t launch_fwd_counting(const FwdParams& p, int D, bool causal, hipStream_t stream) {
   if (!p.events) return hipErrorInvalidValue;
+  // the one-pass short-sequence kernel makes no rescale test: nothing to count
+  if (p.S <= kShortMaxS) return launch_fwd_short(p, D, causal, stream);
   if (D == 128)
     return causal ? launch_fwd_t<128, true, true>(p, stream) : launch_fwd_t<128, false, true>(p, stream);
   if (D == 64)

@@ -67,6 +67,15 @@ int check_bwd_args(const void* q, const void* k, const void* v, const void* o, c
 hipError_t launch_fwd(const FwdParams& p, int D, bool causal, hipStream_t stream);
 hipError_t launch_fwd_counting(const FwdParams& p, int D, bool causal, hipStream_t stream);
 hipError_t launch_bwd(const BwdParams& p, int D, bool causal, unsigned phases, hipStream_t stream);
+
+// Sequences of at most kShortMaxS keys take the one-pass short-sequence
+// forward (attn_fwd_short.hip): the whole row of scores in registers, exact
+// row maxima, no conditional rescale.  (Measured: faster than the ping-pong
+// kernel up to 128 keys -- 16.4 against 23.7 us for 320 causal heads of 128
+// -- and slower at 256 keys, where the one-pass kernel's 128 KiB of LDS and
+// one wave per SIMD leave the chip underused: 46 against 39 us.)
+constexpr int kShortMaxS = 128;
+hipError_t launch_fwd_short(const FwdParams& p, int D, bool causal, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdParams& p, int D, bool causal, hipStream_t stream);
 
 }  // namespace attn

@@ -50,6 +50,8 @@ def _check_scaled_bound(bits, causal, scale, what):
         r = np.stack([ref[hd][i] for hd in range(B * H)]).reshape(B, H, S, D)
         bound = max(P.GRAD_MAX, 2.0 ** -7 * np.abs(r).max())
         err = np.abs(got[i] - r).max()
+        print("%s %s max err %.3e (plain bound %.1e, scaled bound %.3e, max|ref| %.3e)" % (
+            what, name, err, P.GRAD_MAX, bound, np.abs(r).max()))
         assert np.isfinite(err) and err <= bound, "%s %s err %.3e > %.3e" % (
             what, name, err, bound)
 

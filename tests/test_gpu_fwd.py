@@ -27,10 +27,36 @@ def test_tiny_workload(causal):
 
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("S", [1, 17, 64, 130, 1000])
+@pytest.mark.parametrize("S", [1, 17, 64, 128, 130, 256, 257, 1000])
 def test_ragged_lengths(S, D, causal):
+    """S <= 128 runs the one-pass short-sequence kernel; S = 130, 256 and 257
+    take the long-sequence kernel's first (partial) steps."""
     err = _full_case(1, 3, S, D, causal, seed=1000 + S + D + int(causal))
     P.assert_fwd_ok(err, "S=%d D=%d causal=%s" % (S, D, causal))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_short_sequence_many_blocks(causal):
+    """Short-sequence kernel with many workgroups: 150 heads of 100 rows (one
+    128-row block each, the last 28 rows idle), every element against the
+    oracle."""
+    err = _full_case(3, 50, 100, 128, causal, seed=2001 + int(causal))
+    P.assert_fwd_ok(err, "short many blocks causal=%s" % causal)
+
+
+def test_short_sequence_counting_makes_no_tests():
+    """At S <= 128 the counting entry runs the one-pass kernel, which makes no
+    rescale test: zero events, and the same bits as attn_fwd_ex."""
+    import torch
+    import exact_attention_128_amd as A
+    bits = ai.make_inputs(2, 3, 120, 128, 2002, stress=True)
+    dev = torch.device("cuda", 0)
+    q, k, v = (ai.to_torch_bf16(bits[n], dev) for n in ("q", "k", "v"))
+    o, lse, tests, resc = A.fwd_rescale_events(q, k, v, causal=True, scale=0.09, rescale_log2=0.0)
+    o2, lse2 = A.fwd(q, k, v, causal=True, scale=0.09, rescale_log2=0.0)
+    torch.cuda.synchronize()
+    assert tests == 0 and resc == 0
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16)) and torch.equal(lse, lse2)
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -52,8 +78,10 @@ def test_multi_block_lengths(D, causal):
     P.assert_fwd_ok(err, "S=1500 D=%d causal=%s" % (D, causal))
 
 
-@pytest.mark.parametrize("scale", [1.0, -0.09, 0.0, 0.5])
+@pytest.mark.parametrize("scale", [1.0, -0.09, 0.0, 0.5, 16.0])
 def test_scale_values(scale):
+    """Off-standard scales, up to 16 (scores of a few hundred, rows dominated by
+    one or two keys: far inside the fp32 range the header requires)."""
     for causal in (False, True):
         err = _full_case(1, 2, 190, 128, causal, seed=90, scale=scale)
         P.assert_fwd_ok(err, "scale=%g causal=%s" % (scale, causal))
