@@ -79,6 +79,101 @@ def fwd_flops(B, H, S, D, causal):
     return f / 2 if causal else f
 
 
+def oracle_fwd_sample(w, bits, budget_s):
+    """Time the fp64 oracle's forward on a bounded sample of one forward
+    workload: the whole problem when it is small, else chunks of 64 query rows
+    spread evenly over the sequence, cycling through the heads, until about
+    budget_s of CPU time.  Returns its algorithmic rate (the GPU path's flop
+    count for the same rows) and what was sampled."""
+    import numpy as np
+    import attn_inputs as ai
+    import oracle
+    B, H, S, D = w.B, w.H, w.S, w.D
+    full = fwd_flops(B, H, S, D, w.causal)
+    if full <= 1e9:
+        f64 = {n: ai.bf16_bits_to_f64(bits[n]) for n in ("q", "k", "v")}
+        t0 = time.perf_counter()
+        oracle.attn_fwd(f64["q"], f64["k"], f64["v"], w.scale, w.causal)
+        dt = time.perf_counter() - t0
+        return {"tflops": round(full / dt / 1e12, 6), "seconds": round(dt, 3),
+                "sample": "whole workload"}
+    q, k, v = (bits[n].reshape(B * H, S, D) for n in ("q", "k", "v"))
+    flops, rows, chunk, t0 = 0.0, 0, 0, time.perf_counter()
+    while time.perf_counter() - t0 < budget_s and rows < B * H * S:
+        hd = chunk % (B * H)
+        pos = (np.arange(64, dtype=np.int64) * (S // 64) + (chunk * 7919) % max(1, S // 64)) % S
+        oracle.attn_fwd_rows(ai.bf16_bits_to_f64(q[hd, pos]), pos, ai.bf16_bits_to_f64(k[hd]),
+                             ai.bf16_bits_to_f64(v[hd]), w.scale, w.causal)
+        flops += oracle.rows_flops(pos, S, D, w.causal)
+        rows += 64
+        chunk += 1
+    dt = time.perf_counter() - t0
+    return {"tflops": round(flops / dt / 1e12, 6), "seconds": round(dt, 3),
+            "sample": "%d query rows (64-row chunks spread over the sequence, %d heads) of %d" % (
+                rows, min(chunk, B * H), B * H * S)}
+
+
+def _grids(w):
+    """Work-items of each kernel's 1-D grid for workload w (as the library
+    launches them), keyed by kernel family."""
+    bh, S, D = w.B * w.H, w.S, w.D
+    g = {"attn_bwd_dq_kernel": bh * (-(-S // 256)) * 512,
+         "attn_bwd_main_kernel": bh * (-(-S // 128)) * 256,
+         "attn_bwd_pre_kernel": min(-(-(bh * (-(-S // 64)) * 64 * (D // 8)) // 256), 1024) * 256}
+    if S <= 128:
+        g["attn_fwd_short_kernel"] = bh * 256
+    else:
+        g["attn_fwd_kernel"] = bh * (-(-S // 256)) * 512
+    return g
+
+
+# share of a workload's algorithmic flops credited to each kernel (the dK/dV
+# kernel does four of the backward's five products, the dQ kernel the fifth)
+_CREDIT = {"attn_fwd_kernel": ("fwd", 1.0), "attn_fwd_short_kernel": ("fwd", 1.0),
+           "attn_bwd_main_kernel": ("bwd", 0.8), "attn_bwd_dq_kernel": ("bwd", 0.2)}
+
+
+def trace_summary(path):
+    """Markdown summary of a rocprofv3 kernel-trace CSV (--kernel-trace
+    --output-format csv): one row per (kernel, grid size), named by the
+    workload whose launch has that grid, with mean / median / min / max
+    duration and, for the attention kernels, the algorithmic rate and the
+    fraction of the dense bf16 peak computed from the trace's mean."""
+    import csv
+    import statistics
+    import attn_inputs as ai
+    rows = {}
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            name = r["Kernel_Name"]
+            dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3   # us
+            rows.setdefault((name, int(r["Grid_Size_X"])), []).append(dur)
+    total = sum(sum(v) for v in rows.values())
+    out = ["| Kernel | Workload | Grid (work-items) | Calls | Mean (us) | Median (us) | Min (us) "
+           "| Max (us) | Share | Algorithmic TFLOPS (mean) | Fraction of 2516.6 |",
+           "|---|---|---|---|---|---|---|---|---|---|---|"]
+    for (name, grid), d in sorted(rows.items(), key=lambda kv: -sum(kv[1])):
+        fam = name.split("<")[0].split("::")[-1].strip()
+        targs = name.split("<")[1].split(">")[0].split(",") if "<" in name else []
+        wl, tf, frac = "", "", ""
+        for w in ai.WORKLOADS.values():
+            if fam.startswith("attn_") and targs and int(targs[0]) == w.D and \
+                    (len(targs) < 2 or targs[1].strip() == ("true" if w.causal else "false")) and \
+                    _grids(w).get(fam) == grid and (fam.startswith("attn_fwd") or w.backward):
+                wl = w.name
+                if fam in _CREDIT and (len(targs) < 3 or targs[2].strip() in ("false", "2")):
+                    kind, share = _CREDIT[fam]
+                    f = fwd_flops(w.B, w.H, w.S, w.D, w.causal) * (2.5 if kind == "bwd" else 1.0)
+                    t = share * f / (statistics.mean(d) * 1e-6) / 1e12
+                    tf, frac = "%.1f" % t, "%.4f" % (t / PEAK_BF16_TFLOPS)
+                break
+        shown = name if len(name) <= 100 else name[:60] + " ... (library kernel)"
+        out.append("| `%s` | %s | %d | %d | %.1f | %.1f | %.1f | %.1f | %.1f%% | %s | %s |" % (
+            shown, wl or "-", grid, len(d), statistics.mean(d), statistics.median(d), min(d),
+            max(d), 100.0 * sum(d) / total, tf, frac))
+    return "\n".join(out)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -88,13 +183,21 @@ def main():
     ap.add_argument("--no-legs", action="store_true", help="skip the forward-only legs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="target CPU time for the oracle sample")
+                    help="target CPU time for the oracle sample of the step's workload")
+    ap.add_argument("--cpu-leg-seconds", type=float, default=2.0,
+                    help="target CPU time for the oracle sample of each forward leg")
     ap.add_argument("--only", default=None,
                     help="profiling driver: run one workload's kernels --steps times after "
                          "--warmup runs and exit (a workload name, 'copy' for a plain "
                          "1 GiB device copy that calibrates the HBM byte counters, or 'gemm' "
                          "for the bf16 8192^3 library GEMM that calibrates the MFMA clock)")
+    ap.add_argument("--trace-summary", default=None, metavar="KERNEL_TRACE_CSV",
+                    help="print a per-workload markdown summary of a rocprofv3 kernel-trace "
+                         "CSV and exit (no GPU needed)")
     args = ap.parse_args()
+    if args.trace_summary is not None:
+        print(trace_summary(args.trace_summary))
+        return
     if args.only is not None:
         run_only(args)
         return
@@ -131,15 +234,17 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    sev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t_wall = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
+    sev[0].record(stream)
+    for i in range(args.steps):
         step()
-    e1.record(stream)
+        sev[i + 1].record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
-    ms_step = e0.elapsed_time(e1) / args.steps
+    ms_step = sev[0].elapsed_time(sev[args.steps]) / args.steps
+    ms_step_median = float(np.median([sev[i].elapsed_time(sev[i + 1])
+                                      for i in range(args.steps)]))
     f_fwd = fwd_flops(B, H, S, D, causal)
     f_bwd = 2.5 * f_fwd
     value = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
@@ -147,15 +252,24 @@ def main():
                                                           1e3 * t_wall / args.steps))
 
     def time_launches(fn, n):
+        """Mean launch time in ms over n back-to-back launches (HIP events on the
+        launch stream); the per-launch times go to `laps` for the median."""
         fn()
         torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(n):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        ev[0].record(stream)
+        for i in range(n):
             fn()
-        b.record(stream)
+            ev[i + 1].record(stream)
         torch.cuda.synchronize()
-        return a.elapsed_time(b) / n
+        t = [ev[i].elapsed_time(ev[i + 1]) for i in range(n)]
+        laps.append(t)
+        return ev[0].elapsed_time(ev[n]) / n
+
+    laps = []
+
+    def last_median():
+        return float(np.median(laps[-1]))
 
     # The dominant kernel is the backward's dK/dV kernel (run PRE once so the
     # workspace holds the row statistics).  Its algorithmic work is four of the
@@ -166,11 +280,15 @@ def main():
     n_rep = max(args.steps, 10)
     ms_main = time_launches(lambda: A.bwd_out(q, k, v, o, lse, do, dq, dk, dv, ws, causal=causal,
                                               scale=scale, phases=A.BWD_MAIN), n_rep)
+    med_main = last_median()
     ms_dq = time_launches(lambda: A.bwd_out(q, k, v, o, lse, do, dq, dk, dv, ws, causal=causal,
                                             scale=scale, phases=A.BWD_DQ), n_rep)
+    med_dq = last_median()
     ms_fwd = time_launches(lambda: A.fwd_out(q, k, v, o, lse, causal=causal, scale=scale), n_rep)
+    med_fwd = last_median()
     ms_bwd = time_launches(lambda: A.bwd_out(q, k, v, o, lse, do, dq, dk, dv, ws, causal=causal,
                                              scale=scale), n_rep)
+    med_bwd = last_median()
     main_tflops = 0.8 * f_bwd / (ms_main * 1e-3) / 1e12
     dq_alg_tflops = 0.2 * f_bwd / (ms_dq * 1e-3) / 1e12
     dq_exec_tflops = 0.6 * f_bwd / (ms_dq * 1e-3) / 1e12
@@ -178,7 +296,17 @@ def main():
         "bwd total %.3f ms" % (ms_main, main_tflops, ms_dq, dq_exec_tflops, ms_fwd, ms_bwd))
 
     legs = {}
+    cpu_legs = {}
     fwd_roof = None
+    gemm_tflops = None
+    if not args.no_cpu_baseline:
+        import oracle
+        try:
+            cores = len(os.sched_getaffinity(0))
+        except AttributeError:
+            cores = os.cpu_count() or 1
+        cores = min(cores, int(os.environ.get("OMP_NUM_THREADS", cores)))
+        oracle.set_threads(cores)
     if not args.no_legs:
         del q, k, v, do, o, lse, dq, dk, dv, ws
         torch.cuda.empty_cache()
@@ -192,17 +320,22 @@ def main():
                 A.fwd_out(lq, lk, lv, lo, ll, causal=lw.causal, scale=lw.scale)
             ms = time_launches(lambda: A.fwd_out(lq, lk, lv, lo, ll, causal=lw.causal,
                                                  scale=lw.scale), n_rep)
+            med = last_median()
             fl = fwd_flops(lw.B, lw.H, lw.S, lw.D, lw.causal)
             tf = fl / (ms * 1e-3) / 1e12
             # algorithmic HBM bytes: Q, K, V read and O written (bf16), LSE (fp32)
             nbytes = 8.0 * lw.B * lw.H * lw.S * lw.D + 4.0 * lw.B * lw.H * lw.S
             gbs = nbytes / (ms * 1e-3) / 1e9
             legs[name] = {"shape": [lw.B, lw.H, lw.S, lw.D], "causal": lw.causal,
-                          "ms": round(ms, 4), "tflops": round(tf, 2),
+                          "ms": round(ms, 4), "median_ms": round(med, 4), "tflops": round(tf, 2),
                           "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                          "frac_peak_median": round(fl / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                           "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
             log("fwd leg %s: %.4f ms  %.1f TFLOPS (%.1f%%)  %.1f GB/s algorithmic HBM" % (
                 name, ms, tf, 100 * tf / PEAK_BF16_TFLOPS, gbs))
+            if not args.no_cpu_baseline:
+                cpu_legs[name] = oracle_fwd_sample(lw, lb, args.cpu_leg_seconds)
+                log("  cpu oracle %s: %s" % (name, cpu_legs[name]))
             if lw.causal:
                 # untimed: how often the conditional rescale fires (the counting
                 # forward, attn_fwd_rescale_events), at the default threshold
@@ -228,9 +361,10 @@ def main():
             torch.matmul(ga, gb, out=gc)
         ms = time_launches(lambda: torch.matmul(ga, gb, out=gc), n_rep)
         tf = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+        gemm_tflops = tf
         legs["library_gemm"] = {"op": "torch.matmul bf16 8192x8192x8192 (hipBLASLt)",
-                                "ms": round(ms, 4), "tflops": round(tf, 1),
-                                "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+                                "ms": round(ms, 4), "median_ms": round(last_median(), 4),
+                                "tflops": round(tf, 1), "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
         log("library GEMM (hipBLASLt bf16 8192^3): %.4f ms  %.1f TFLOPS (%.1f%%)" % (
             ms, tf, 100 * tf / PEAK_BF16_TFLOPS))
         del ga, gb, gc
@@ -238,18 +372,13 @@ def main():
         c3 = legs["fwd_causal_s8k"]
         fwd_roof = {"kernel": "attn_fwd_kernel<128,causal>", "workload": "fwd_causal_s8k",
                     "bound": "mfma", "achieved": c3["tflops"], "peak": PEAK_BF16_TFLOPS,
-                    "unit": "TFLOP/s", "frac": c3["frac_peak"],
+                    "unit": "TFLOP/s", "frac": c3["frac_peak"], "ms": c3["ms"],
+                    "median_ms": c3["median_ms"], "frac_median": c3["frac_peak_median"],
+                    "frac_vs_library_gemm": round(c3["tflops"] / gemm_tflops, 4),
                     "traffic": measured_traffic("fwd_causal_s8k", FWD_TRAFFIC, FWD_TRAFFIC_SOURCES)}
 
     cpu = None
     if not args.no_cpu_baseline:
-        import oracle
-        try:
-            cores = len(os.sched_getaffinity(0))
-        except AttributeError:
-            cores = os.cpu_count() or 1
-        cores = min(cores, int(os.environ.get("OMP_NUM_THREADS", cores)))
-        oracle.set_threads(cores)
         qs, ks, vs, dos = (bits[n].reshape(B * H, S, D) for n in ("q", "k", "v", "do"))
         t0 = time.perf_counter()
         heads = 0
@@ -262,7 +391,8 @@ def main():
         cpu = {"value": round(heads * per_head / dt / 1e12, 6), "unit": "TFLOPS",
                "cores": oracle.max_threads(), "kind": "oracle",
                "sample": "%d of %d heads of the workload, fp64 forward+backward per head, "
-                         "%.1f s" % (heads, B * H, dt)}
+                         "%.1f s" % (heads, B * H, dt),
+               "per_config": cpu_legs}
         log("cpu oracle: %s" % cpu)
 
     out = {
@@ -283,13 +413,22 @@ def main():
         "roofline": {"kernel": "attn_bwd_main_kernel<128,causal>", "bound": "mfma",
                      "achieved": round(main_tflops, 1), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(main_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic(w.name), "ms": round(ms_main, 4)},
+                     "traffic": measured_traffic(w.name), "ms": round(ms_main, 4),
+                     "median_ms": round(med_main, 4),
+                     "frac_median": round(0.8 * f_bwd / (med_main * 1e-3) / 1e12 /
+                                          PEAK_BF16_TFLOPS, 4),
+                     "frac_vs_library_gemm": (round(main_tflops / gemm_tflops, 4)
+                                              if gemm_tflops else None)},
         "dq_kernel": {"kernel": "attn_bwd_dq_kernel<128,causal>", "ms": round(ms_dq, 4),
+                      "median_ms": round(med_dq, 4),
                       "algorithmic_tflops": round(dq_alg_tflops, 1),
                       "executed_tflops": round(dq_exec_tflops, 1),
                       "executed_frac": round(dq_exec_tflops / PEAK_BF16_TFLOPS, 4)},
+        "ms_per_step_median": round(ms_step_median, 4),
         "fwd_ms": round(ms_fwd, 4),
+        "fwd_median_ms": round(med_fwd, 4),
         "bwd_ms": round(ms_bwd, 4),
+        "bwd_median_ms": round(med_bwd, 4),
         "fwd_tflops": round(f_fwd / (ms_fwd * 1e-3) / 1e12, 1),
         "bwd_tflops": round(f_bwd / (ms_bwd * 1e-3) / 1e12, 1),
         "fwd_roofline": fwd_roof,
