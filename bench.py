@@ -174,6 +174,68 @@ def trace_summary(path):
     return "\n".join(out)
 
 
+SWEEP_TAUS = (0.0, 8.0, 16.0, 32.0, 64.0)
+SWEEP_POLYS = (0, 8, 4)
+
+
+def sweep_policy(args):
+    """Time the long-sequence forward at every (rescale threshold, exponential
+    policy) pair on each forward workload of at least 2048 keys (and the
+    backward workload's forward), interleaving the pairs over three rounds so
+    a drifting clock favours none; prints a markdown table of the median of
+    the per-round means and one JSON line with the winner per workload."""
+    import numpy as np
+    import torch
+    import attn_inputs as ai
+    import exact_attention_128_amd as A
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    names = ("fwd_s2k", "bwd_causal_s4k", "fwd_causal_s8k", "fwd_stress_s16k")
+    pairs = [(t, p) for p in SWEEP_POLYS for t in SWEEP_TAUS]
+    result = {}
+    lines = ["| Workload | tau | exp poly every | ms (median of 3 rounds x %d launches) | TFLOPS |"
+             " vs library choice |" % args.steps, "|---|---|---|---|---|---|"]
+    for name in names:
+        w = ai.WORKLOADS[name]
+        bits = ai.make_inputs(w.B, w.H, w.S, w.D, w.seed, stress=w.stress)
+        q, k, v = (ai.to_torch_bf16(bits[n], dev) for n in ("q", "k", "v"))
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=dev)
+        times = {pr: [] for pr in pairs}
+        for _ in range(3):
+            for (tau, poly) in pairs:
+                run = lambda: A.fwd_out(q, k, v, o, lse, causal=w.causal, scale=w.scale,
+                                        rescale_log2=tau, exp_poly_every=poly)
+                for _ in range(args.warmup):
+                    run()
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                for _ in range(args.steps):
+                    run()
+                b.record(stream)
+                torch.cuda.synchronize()
+                times[(tau, poly)].append(a.elapsed_time(b) / args.steps)
+        fl = fwd_flops(w.B, w.H, w.S, w.D, w.causal)
+        med = {pr: float(np.median(t)) for pr, t in times.items()}
+        lib_choice = A.default_policy(w.D, w.causal, w.S)
+        best = min(med, key=med.get)
+        result[name] = {"best": {"tau": best[0], "exp_poly_every": best[1], "ms": round(med[best], 4)},
+                        "library_choice": {"tau": lib_choice[0], "exp_poly_every": lib_choice[1],
+                                           "ms": round(med[lib_choice], 4)},
+                        "ms": {"%g/%d" % pr: round(t, 4) for pr, t in med.items()}}
+        for pr in pairs:
+            lines.append("| %s | %g | %d | %.4f | %.1f | %+.1f%% |" % (
+                name, pr[0], pr[1], med[pr], fl / (med[pr] * 1e-3) / 1e12,
+                100.0 * (med[pr] / med[lib_choice] - 1.0)))
+        log("sweep %s: best tau %g poly %d %.4f ms; library choice %s %.4f ms" % (
+            name, best[0], best[1], med[best], lib_choice, med[lib_choice]))
+        del q, k, v, o, lse
+        torch.cuda.empty_cache()
+    print("\n".join(lines), flush=True)
+    print(json.dumps({"sweep": result}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -194,7 +256,14 @@ def main():
     ap.add_argument("--trace-summary", default=None, metavar="KERNEL_TRACE_CSV",
                     help="print a per-workload markdown summary of a rocprofv3 kernel-trace "
                          "CSV and exit (no GPU needed)")
+    ap.add_argument("--sweep-policy", action="store_true",
+                    help="time the forward at every (rescale threshold, exponential policy) "
+                         "pair on the forward workloads and print the table (uses --steps, "
+                         "--warmup per pair and round)")
     args = ap.parse_args()
+    if args.sweep_policy:
+        sweep_policy(args)
+        return
     if args.trace_summary is not None:
         print(trace_summary(args.trace_summary))
         return
@@ -338,10 +407,10 @@ def main():
                 log("  cpu oracle %s: %s" % (name, cpu_legs[name]))
             if lw.causal:
                 # untimed: how often the conditional rescale fires (the counting
-                # forward, attn_fwd_rescale_events), at the default threshold
-                # 2^32 and at FA4's 2^8
+                # forward, attn_fwd_rescale_events), at the library's threshold
+                # 2^64, at 2^32 and at FA4's 2^8
                 ev = {}
-                for tau in (32.0, 8.0):
+                for tau in (64.0, 32.0, 8.0):
                     _, _, tests, fired = A.fwd_rescale_events(lq, lk, lv, causal=lw.causal,
                                                               scale=lw.scale, rescale_log2=tau)
                     ev["tau%d" % tau] = {"tests": tests, "fired": fired,

@@ -19,7 +19,7 @@ from . import _lib
 from ._lib import AttnError, load, library_path  # noqa: F401
 
 __all__ = ["fwd", "bwd", "fwd_out", "fwd_rescale_events", "bwd_out", "bwd_workspace_size",
-           "bwd_noalloc_out", "AttnError", "load", "library_path"]
+           "bwd_noalloc_out", "default_policy", "AttnError", "load", "library_path"]
 
 
 def _check(t, name, shape=None, device=None):
@@ -58,8 +58,11 @@ def _stream(device):
 
 
 def fwd_out(q, k, v, o, lse, causal: bool = False, scale: float | None = None,
-            rescale_log2: float | None = None) -> None:
-    """Forward into caller-provided o (bf16 [B,H,S,D]) and lse (fp32 [B,H,S])."""
+            rescale_log2: float | None = None, exp_poly_every: int | None = None) -> None:
+    """Forward into caller-provided o (bf16 [B,H,S,D]) and lse (fp32 [B,H,S]).
+
+    rescale_log2 / exp_poly_every override the per-shape softmax policy
+    (attn_fwd_ex / attn_fwd_policy); None keeps the library's choice."""
     _check(q, "q")
     B, H, S, D = q.shape
     _check(k, "k", q.shape, q.device)
@@ -69,7 +72,14 @@ def fwd_out(q, k, v, o, lse, causal: bool = False, scale: float | None = None,
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     st = _stream(q.device)
-    if rescale_log2 is None:
+    if exp_poly_every is not None:
+        if rescale_log2 is None:
+            rescale_log2 = default_policy(D, causal, S)[0]
+        rc = _lib.load().attn_fwd_policy(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                         lse.data_ptr(), B, H, S, D, float(scale),
+                                         int(bool(causal)), float(rescale_log2),
+                                         int(exp_poly_every), st)
+    elif rescale_log2 is None:
         rc = _lib.load().attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                   lse.data_ptr(), B, H, S, D, float(scale), int(bool(causal)), st)
     else:
@@ -80,15 +90,26 @@ def fwd_out(q, k, v, o, lse, causal: bool = False, scale: float | None = None,
 
 
 def fwd(q, k, v, causal: bool = False, scale: float | None = None,
-        rescale_log2: float | None = None):
+        rescale_log2: float | None = None, exp_poly_every: int | None = None):
     """Returns (O bf16 [B,H,S,D], LSE fp32 [B,H,S])."""
     import torch
     _check(q, "q")
     B, H, S, D = q.shape
     o = torch.empty_like(q)
     lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
-    fwd_out(q, k, v, o, lse, causal=causal, scale=scale, rescale_log2=rescale_log2)
+    fwd_out(q, k, v, o, lse, causal=causal, scale=scale, rescale_log2=rescale_log2,
+            exp_poly_every=exp_poly_every)
     return o, lse
+
+
+def default_policy(D: int, causal: bool, S: int):
+    """(rescale_log2, exp_poly_every) that attn_fwd picks for this shape."""
+    import ctypes
+    tau, poly = ctypes.c_float(), ctypes.c_int()
+    rc = _lib.load().attn_fwd_default_policy(int(D), int(bool(causal)), int(S), ctypes.byref(tau),
+                                             ctypes.byref(poly))
+    _lib.raise_for(rc, "attn_fwd_default_policy")
+    return float(tau.value), int(poly.value)
 
 
 def fwd_rescale_events(q, k, v, causal: bool = False, scale: float | None = None,

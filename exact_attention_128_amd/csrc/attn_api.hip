@@ -53,8 +53,32 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// The forward's softmax policy for a shape: the rescale threshold tau (log2
+// units) and the share of exponentials computed by the polynomial on the FMA
+// pipe (poly: every poly-th of a lane, 0 = none) -- the two knobs FA4 tunes
+// per hardware generation (Tencent Cloud article, section 7; QbitAI, "三招").
+// The table holds the measured winner of a sweep of tau in {0, 8, 16, 32,
+// 64} x poly in {0, 8, 4} over the four long forward workloads on MI355X
+// (bench.py --sweep-policy): no polynomial share ever won (+2 to +8 % time:
+// its eight VALU operations per element cost the softmax wave more issue
+// slots than the transcendental unit frees), and tau = 64 was best or within
+// 0.1 % of it on every workload (rising maxima: -0.9 % against tau = 32,
+// -12 % against FA4's 8), so one setting serves every shape.  At tau = 64 a
+// weight stays below 2^64 and a row's sums below 2^81, far inside fp32.
+struct FwdPolicy {
+  float tau;
+  int poly;
+};
+
+FwdPolicy select_policy(int D, int causal, int S) {
+  (void)D;
+  (void)causal;
+  (void)S;
+  return FwdPolicy{64.0f, 0};
+}
+
 int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-             int S, int D, float scale, int causal, float tau, attn_stream_t stream,
+             int S, int D, float scale, int causal, float tau, int poly, attn_stream_t stream,
              unsigned long long* events = nullptr, bool counting = false) {
   if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
   if (counting && !events) return ATTN_ERR_NULL;
@@ -66,6 +90,8 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
   if (counting && !aligned(events, 8)) return ATTN_ERR_ALIGN;
   if (!scale_ok(scale)) return ATTN_ERR_SCALE;
   if (!(tau >= 0.0f && tau <= 64.0f)) return ATTN_ERR_SCALE;
+  if (poly != 0 && poly != 4 && poly != 8) return ATTN_ERR_UNSUPPORTED;
+  if (counting && poly != 0) return ATTN_ERR_UNSUPPORTED;
 
   attn::FwdParams p{};
   p.q = static_cast<const uint16_t*>(q);
@@ -87,7 +113,7 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
   p.events = events;
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   return hip_status(counting ? attn::launch_fwd_counting(p, D, causal != 0, st)
-                             : attn::launch_fwd(p, D, causal != 0, st));
+                             : attn::launch_fwd(p, D, causal != 0, poly, st));
 }
 
 }  // namespace
@@ -116,20 +142,40 @@ extern "C" {
 
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
              int S, int D, float scale, int causal, attn_stream_t stream) {
-  return fwd_impl(q, k, v, o, lse, B, H, S, D, scale, causal, 32.0f, stream);
+  const FwdPolicy pol = select_policy(D, causal, S);
+  return fwd_impl(q, k, v, o, lse, B, H, S, D, scale, causal, pol.tau, pol.poly, stream);
 }
 
 int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                 int S, int D, float scale, int causal, float rescale_log2,
                 attn_stream_t stream) {
-  return fwd_impl(q, k, v, o, lse, B, H, S, D, scale, causal, rescale_log2, stream);
+  const FwdPolicy pol = select_policy(D, causal, S);
+  return fwd_impl(q, k, v, o, lse, B, H, S, D, scale, causal, rescale_log2, pol.poly, stream);
+}
+
+int attn_fwd_policy(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                    int H, int S, int D, float scale, int causal, float rescale_log2,
+                    int exp_poly_every, attn_stream_t stream) {
+  return fwd_impl(q, k, v, o, lse, B, H, S, D, scale, causal, rescale_log2, exp_poly_every,
+                  stream);
+}
+
+int attn_fwd_default_policy(int D, int causal, int S, float* rescale_log2, int* exp_poly_every) {
+  if (!rescale_log2 || !exp_poly_every) return ATTN_ERR_NULL;
+  if (D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
+  if (S < 1) return ATTN_ERR_SHAPE;
+  const FwdPolicy pol = select_policy(D, causal, S);
+  *rescale_log2 = pol.tau;
+  *exp_poly_every = pol.poly;
+  return ATTN_OK;
 }
 
 int attn_fwd_rescale_events(const void* q, const void* k, const void* v, void* o, float* lse,
                             int B, int H, int S, int D, float scale, int causal,
                             float rescale_log2, unsigned long long* events,
                             attn_stream_t stream) {
-  return fwd_impl(q, k, v, o, lse, B, H, S, D, scale, causal, rescale_log2, stream, events, true);
+  return fwd_impl(q, k, v, o, lse, B, H, S, D, scale, causal, rescale_log2, 0, stream, events,
+                  true);
 }
 
 size_t attn_bwd_workspace_size(int B, int H, int S, int D) {

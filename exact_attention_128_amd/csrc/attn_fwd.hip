@@ -86,10 +86,36 @@ struct FwdTile {
   static constexpr int VPIECE = 2 * DB * (BC / 16);
 };
 
+// FA4's software exponential (Tencent Cloud article, section 7: Cody-Waite
+// range reduction and a cubic on the FMA units, for a share of the
+// elements).  In base 2 the range reduction is exact: x = n + f with
+// n = floor(x), f in [0, 1); 2^f is a cubic fitted here for minimax relative
+// error on [0, 1) with p(0) = 1 exactly (so integer x give exact powers of
+// two), max relative error 8.6e-5 -- 23 times below the 2^-9 rounding that P
+// undergoes next; 2^n is applied by v_ldexp_f32.  The clamp sends -inf
+// (masked keys) and anything below -160 to an exact 0 through ldexp's
+// underflow; a finite x past 128 overflows to +inf exactly as v_exp_f32
+// does, which the rescale test catches.
+constexpr float kExpP1 = 0.6951172947883606f;
+constexpr float kExpP2 = 0.22764353454113007f;
+constexpr float kExpP3 = 0.077068030834198f;
+
+__device__ __forceinline__ float exp2_poly(float x) {
+  x = fmaxf(x, -160.0f);
+  const float n = __builtin_floorf(x);
+  const float f = x - n;
+  const float p = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(kExpP3, f, kExpP2), f, kExpP1), f,
+                                 1.0f);
+  return __builtin_ldexpf(p, (int)n);
+}
+
 // COUNT: the diagnostic instantiation behind attn_fwd_rescale_events, which
 // also counts the rescale tests and the rescales (same arithmetic, same
 // results; the production kernels are the COUNT = false ones).
-template <int D, bool CAUSAL, bool COUNT = false>
+// POLY: exponential policy -- 0: every exponential on the hardware unit
+// (v_exp_f32); 4 or 8: every POLY-th exponential of a lane (a fixed column
+// subset of each score tile, 25 % or 12.5 % of them) by exp2_poly instead.
+template <int D, bool CAUSAL, bool COUNT = false, int POLY = 0>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(FwdParams p) {
   using T = FwdTile<D>;
@@ -338,7 +364,9 @@ void attn_fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) e[i][r] = __builtin_amdgcn_exp2f(x[i][r] - mx);
+      for (int r = 0; r < 16; ++r)
+        e[i][r] = (POLY > 0 && r % (POLY > 0 ? POLY : 1) == 0) ? exp2_poly(x[i][r] - mx)
+                                                                : __builtin_amdgcn_exp2f(x[i][r] - mx);
     __builtin_amdgcn_sched_barrier(0);
     float t[8];
 #pragma unroll
@@ -531,7 +559,7 @@ void attn_fwd_kernel(FwdParams p) {
   }
 }
 
-template <int D, bool CAUSAL, bool COUNT = false>
+template <int D, bool CAUSAL, bool COUNT = false, int POLY = 0>
 static hipError_t launch_fwd_t(const FwdParams& p0, hipStream_t stream) {
   constexpr int NW = 8;
   FwdParams p = p0;
@@ -541,14 +569,24 @@ static hipError_t launch_fwd_t(const FwdParams& p0, hipStream_t stream) {
   const long grid = (long)p.bh * p.nqb;
   if (grid <= 0 || grid * NW * 64 > 0xffffffffL) return hipErrorInvalidConfiguration;
   void* args[] = {&p};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_kernel<D, CAUSAL, COUNT>),
+  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_kernel<D, CAUSAL, COUNT, POLY>),
                          dim3((unsigned)grid), dim3(NW * 64), args, 0, stream);
 }
 
-hipError_t launch_fwd(const FwdParams& p, int D, bool causal, hipStream_t stream) {
+template <int D, bool CAUSAL>
+static hipError_t launch_fwd_poly(const FwdParams& p, int poly, hipStream_t stream) {
+  if (poly == 0) return launch_fwd_t<D, CAUSAL, false, 0>(p, stream);
+  if (poly == 4) return launch_fwd_t<D, CAUSAL, false, 4>(p, stream);
+  if (poly == 8) return launch_fwd_t<D, CAUSAL, false, 8>(p, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_fwd(const FwdParams& p, int D, bool causal, int poly, hipStream_t stream) {
   if (p.S <= kShortMaxS) return launch_fwd_short(p, D, causal, stream);
-  if (D == 128) return causal ? launch_fwd_t<128, true>(p, stream) : launch_fwd_t<128, false>(p, stream);
-  if (D == 64) return causal ? launch_fwd_t<64, true>(p, stream) : launch_fwd_t<64, false>(p, stream);
+  if (D == 128)
+    return causal ? launch_fwd_poly<128, true>(p, poly, stream) : launch_fwd_poly<128, false>(p, poly, stream);
+  if (D == 64)
+    return causal ? launch_fwd_poly<64, true>(p, poly, stream) : launch_fwd_poly<64, false>(p, poly, stream);
   return hipErrorInvalidValue;
 }
 

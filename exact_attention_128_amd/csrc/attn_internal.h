@@ -64,7 +64,9 @@ int check_bwd_args(const void* q, const void* k, const void* v, const void* o, c
                    const void* dout, const void* dq, const void* dk, const void* dv, int B,
                    int H, int S, int D, float scale);
 
-hipError_t launch_fwd(const FwdParams& p, int D, bool causal, hipStream_t stream);
+// poly: the exponential policy of the long-sequence kernel (0, 4 or 8; see
+// attn_fwd.hip); the short-sequence kernel always uses the hardware unit.
+hipError_t launch_fwd(const FwdParams& p, int D, bool causal, int poly, hipStream_t stream);
 hipError_t launch_fwd_counting(const FwdParams& p, int D, bool causal, hipStream_t stream);
 hipError_t launch_bwd(const BwdParams& p, int D, bool causal, unsigned phases, hipStream_t stream);
 

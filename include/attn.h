@@ -38,9 +38,9 @@
  *     score as an fp32 dot product multiplied by |scale| * log2(e), so the
  *     inputs must also keep |scale * q_i . k_j| * log2(e) below FLT_MAX
  *     (about 3.4e38) for every visible pair: a score past that overflows to
- *     infinity and the rows it touches come out NaN.  That is the only
- *     data-dependent limit; unit-variance inputs sit some 35 orders of
- *     magnitude inside it.
+ *     infinity and the rows it touches come out NaN.  The one other
+ *     data-dependent limit is |V| < 2^47 for the forward (see attn_fwd);
+ *     unit-variance inputs sit many orders of magnitude inside both.
  *   - Every load stays inside the extent of the tensor it reads (a partial
  *     last tile is zero-filled on chip), so buffers may be allocated to their
  *     exact size with nothing mapped after them.
@@ -87,12 +87,14 @@ enum attn_status {
  *   scale    multiplies the logits before masking and softmax (usually 1/sqrt(D)).
  *   causal   nonzero: key j is visible to query i iff j <= i.
  * The online softmax rescales the running output only when a row's maximum
- * grows by about 32 (log2 units) over the stale maximum it is using (the test
+ * grows by about 64 (log2 units) over the stale maximum it is using (the test
  * is described at attn_fwd_ex), the conditional-rescaling idea of FA4
  * (Tencent Cloud article, section 7): the unnormalised weights stay below
- * 2^32, far inside the fp32 and bf16 exponent range of the sums and the PV
- * product.  The result is the same for every
- * threshold, see attn_fwd_ex.
+ * 2^64 and a row's sums below 2^81, inside the fp32 and bf16 exponent range
+ * of the sums and the PV product as long as |V| < 2^47 (the fp32 output
+ * accumulators hold at most 2^81 * max|V|).  The threshold and the
+ * exponential policy come from a per-shape table (attn_fwd_default_policy);
+ * the result is the same for every threshold, see attn_fwd_ex.
  * Returns ATTN_OK or an attn_status code; nothing is written on error.
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -114,6 +116,36 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
                 int B, int H, int S, int D, float scale, int causal,
                 float rescale_log2, attn_stream_t stream);
+
+/*
+ * Forward with both softmax knobs explicit: the rescale threshold
+ * rescale_log2 in [0, 64] (as attn_fwd_ex) and the exponential policy of FA4
+ * (Tencent Cloud article, section 7: a polynomial exp2 on the FMA units for a
+ * share of the elements, beside the hardware transcendental unit):
+ *   exp_poly_every  0: every exponential on the hardware unit (v_exp_f32);
+ *                   4 or 8: every 4th or 8th exponential of a lane (25 % or
+ *                   12.5 % of them, a fixed column subset of each score
+ *                   tile) by 2^floor(x) * p(x - floor(x)), p a cubic with
+ *                   relative error below 8.6e-5 (23 times below the bf16
+ *                   rounding the weights undergo next).
+ * Every policy yields the same exact result up to rounding.  Sequences of at
+ * most 128 keys take the one-pass short-sequence kernel, which has neither
+ * knob (exact row maxima, hardware exponentials).  Other arguments as
+ * attn_fwd.  Threshold out of range: ATTN_ERR_SCALE; exp_poly_every not 0, 4
+ * or 8: ATTN_ERR_UNSUPPORTED.
+ */
+int attn_fwd_policy(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int H, int S, int D, float scale, int causal,
+                    float rescale_log2, int exp_poly_every, attn_stream_t stream);
+
+/*
+ * The policy attn_fwd picks for a shape (a table of measured winners per
+ * shape; attn_fwd_ex keeps its exponential policy and takes the threshold
+ * from the caller): writes the rescale threshold and the exponential policy
+ * (as attn_fwd_policy).  NULL output: ATTN_ERR_NULL; D not 64 or 128:
+ * ATTN_ERR_HEAD_DIM; S < 1: ATTN_ERR_SHAPE.
+ */
+int attn_fwd_default_policy(int D, int causal, int S, float* rescale_log2, int* exp_poly_every);
 
 /*
  * Diagnostic forward that also counts the conditional-rescale events (the FA4

@@ -14,17 +14,18 @@ import oracle
 O_MAX, O_MEAN, LSE_MAX, GRAD_MAX = 2e-2, 2e-3, 1e-3, 5e-2
 
 
-def gpu_fwd(bits, causal, scale, rescale_log2=None, stream=None):
+def gpu_fwd(bits, causal, scale, rescale_log2=None, stream=None, exp_poly_every=None):
     """Run the forward on cuda:0; returns (O as fp64 numpy, LSE fp64 numpy, O bits)."""
     import torch
     import exact_attention_128_amd as A
     dev = torch.device("cuda", 0)
     q, k, v = (ai.to_torch_bf16(bits[n], dev) for n in ("q", "k", "v"))
+    kw = dict(causal=causal, scale=scale, rescale_log2=rescale_log2, exp_poly_every=exp_poly_every)
     if stream is None:
-        o, lse = A.fwd(q, k, v, causal=causal, scale=scale, rescale_log2=rescale_log2)
+        o, lse = A.fwd(q, k, v, **kw)
     else:
         with torch.cuda.stream(stream):
-            o, lse = A.fwd(q, k, v, causal=causal, scale=scale, rescale_log2=rescale_log2)
+            o, lse = A.fwd(q, k, v, **kw)
         stream.synchronize()
     torch.cuda.synchronize()
     ob = ai.torch_bf16_to_bits(o)

@@ -190,3 +190,17 @@ def test_python_binding_rejects_tensors_on_other_devices():
         A.fwd_out(q, k_other, v, o, lse)
     with pytest.raises(ValueError, match="k is on"):
         A.bwd_out(q, k_other, v, o, lse, do, dq, dk, dv, ws)
+
+
+def test_default_policy_query(lib):
+    tau, poly = ctypes.c_float(), ctypes.c_int()
+    for (D, causal, S) in ((128, 1, 8192), (128, 0, 2048), (64, 1, 16384), (128, 1, 4096)):
+        assert lib.attn_fwd_default_policy(D, causal, S, ctypes.byref(tau), ctypes.byref(poly)) == 0
+        assert 0.0 <= tau.value <= 64.0 and poly.value in (0, 4, 8)
+    assert lib.attn_fwd_default_policy(96, 1, 10, ctypes.byref(tau), ctypes.byref(poly)) == 3
+    assert lib.attn_fwd_default_policy(128, 1, 0, ctypes.byref(tau), ctypes.byref(poly)) == 2
+    assert lib.attn_fwd_default_policy(128, 1, 10, None, ctypes.byref(poly)) == 1
+    pol = lib.attn_fwd_policy
+    assert pol(P, P, P, P, P, 1, 1, 300, 128, 0.1, 1, 8.0, 3, None) == 7     # not 0, 4, 8
+    assert pol(P, P, P, P, P, 1, 1, 300, 128, 0.1, 1, 65.0, 4, None) == 6    # tau range
+    assert pol(P, P, P, P, P + 2, 1, 1, 300, 128, 0.1, 1, 8.0, 4, None) == 4

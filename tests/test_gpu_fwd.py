@@ -115,6 +115,35 @@ def test_rescale_threshold_gives_same_result():
         assert np.all(diff <= bound), "tau=%g vs 0: max diff %.3e" % (tau, diff.max())
 
 
+@pytest.mark.parametrize("poly", [4, 8])
+def test_exp_policies_match_oracle(poly):
+    """FA4's polynomial exp2 for every 4th / 8th exponential: the same result as
+    the hardware exponential, against the oracle, at several thresholds (the
+    rising-maximum input rescales often at low thresholds, so the polynomial
+    also runs on the rescale path) and at D = 64 non-causal."""
+    bits = ai.make_inputs(1, 4, 3000, 128, 45, stress=True)
+    scale = 1.0 / np.sqrt(128)
+    o_ref, lse_ref = P.oracle_fwd_full(bits, True, scale)
+    for tau in (0.0, 8.0, 32.0):
+        o, lse, _ = P.gpu_fwd(bits, True, scale, rescale_log2=tau, exp_poly_every=poly)
+        P.assert_fwd_ok(P.fwd_errors(o, lse, o_ref, lse_ref), "poly=%d tau=%g" % (poly, tau))
+    bits = ai.make_inputs(2, 3, 1500, 64, 46)
+    o, lse, _ = P.gpu_fwd(bits, False, 0.125, exp_poly_every=poly)
+    o_ref, lse_ref = P.oracle_fwd_full(bits, False, 0.125)
+    P.assert_fwd_ok(P.fwd_errors(o, lse, o_ref, lse_ref), "poly=%d D=64" % poly)
+
+
+def test_default_policy_is_the_one_attn_fwd_runs():
+    """attn_fwd gives the same bits as attn_fwd_policy with the policy that
+    attn_fwd_default_policy reports for the shape."""
+    import exact_attention_128_amd as A
+    bits = ai.make_inputs(1, 2, 700, 128, 47)
+    tau, poly = A.default_policy(128, True, 700)
+    _, l1, b1 = P.gpu_fwd(bits, True, 0.1)
+    _, l2, b2 = P.gpu_fwd(bits, True, 0.1, rescale_log2=tau, exp_poly_every=poly)
+    assert np.array_equal(b1, b2) and np.array_equal(l1, l2)
+
+
 def _expected_tests(B, H, S, causal):
     """Rescale tests the kernel makes: one per wave (32 query rows) and 128-key
     step after the wave's first step."""
@@ -184,6 +213,13 @@ def test_full_size_workloads(name):
     err = P.fwd_errors(o, lse, o_ref, lse_ref)
     print(name, err)
     P.assert_fwd_ok(err, name)
+    if w.stress:
+        # the other softmax policy corner on the same oracle: FA4's threshold 8
+        # with every 4th exponential by the polynomial
+        o, lse, _ = P.gpu_fwd(bits, w.causal, w.scale, rescale_log2=8.0, exp_poly_every=4)
+        err = P.fwd_errors(o, lse, o_ref, lse_ref)
+        print(name, "tau 8, poly 4", err)
+        P.assert_fwd_ok(err, name + " tau 8 poly 4")
 
 
 @pytest.mark.parametrize("causal", [False, True])
