@@ -71,6 +71,10 @@ WORKLOADS = {
     "bwd_causal_s4k": Workload("bwd_causal_s4k", 2, 16, 4096, 128, True, backward=True, index=5),
 }
 
+# The FP8 forward measured on the causal long-sequence shape (same seed and
+# draws as fwd_causal_s8k, quantized to E4M3 per tensor).
+FP8_WORKLOAD = Workload("fwd_causal_s8k_fp8", 2, 32, 8192, 128, True, index=3)
+
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round fp32 to bf16, nearest-even; returns the uint16 bit patterns."""
@@ -141,6 +145,84 @@ def make_inputs_chunked(B: int, H: int, S: int, D: int, seed: int, with_dout: bo
     with concurrent.futures.ThreadPoolExecutor(max_workers=max(1, threads)) as ex:
         list(ex.map(fill, range(len(names) * chunks)))
     return {n: a.reshape(B, H, S, D) for n, a in out.items()}
+
+
+# ---- FP8 (OCP E4M3: 1 sign, 4 exponent bits with bias 7, 3 mantissa bits, no
+#      infinities, 0x7f / 0xff are NaN, largest finite 448) for the FP8 forward.
+
+E4M3_MAX = 448.0
+
+
+def f32_to_e4m3_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp32 values to E4M3, nearest-even; returns uint8 codes.  The
+    caller keeps |x| <= 448 (the format has no infinities)."""
+    x = np.ascontiguousarray(x, dtype=np.float32).astype(np.float64)
+    a = np.abs(x)
+    if not np.all(np.isfinite(a)) or a.max(initial=0.0) > E4M3_MAX:
+        raise ValueError("E4M3 input outside [-448, 448]")
+    _, ex = np.frexp(a)                       # a = f * 2^ex, f in [0.5, 1)
+    e = np.maximum(ex - 1, -6)                # unbiased exponent, subnormals share -6
+    q = np.rint(np.ldexp(a, 3 - e))           # significand in units of 2^(e-3), ties to even
+    up = q >= 16                              # rounded up into the next binade
+    e = np.where(up, e + 1, e)
+    q = np.where(up, q / 2, q)
+    normal = q >= 8
+    code = np.where(normal, ((e + 7) << 3) + (q - 8), q).astype(np.int64)
+    code = np.where(a == 0, 0, code)
+    return (code | (np.signbit(x).astype(np.int64) << 7)).astype(np.uint8)
+
+
+def e4m3_bits_to_f64(b: np.ndarray) -> np.ndarray:
+    """Exact value of E4M3 codes (NaN for 0x7f / 0xff)."""
+    b = np.ascontiguousarray(b, dtype=np.uint8).astype(np.int64)
+    E, m = (b >> 3) & 15, b & 7
+    v = np.where(E == 0, np.ldexp(m.astype(np.float64), -9),
+                 np.ldexp((8 + m).astype(np.float64), E - 10))
+    v = np.where((E == 15) & (m == 7), np.nan, v)
+    return np.where(b & 0x80, -v, v)
+
+
+def quantize_e4m3(x: np.ndarray):
+    """Per-tensor scaling to E4M3 (the largest magnitude maps to at most 448):
+    returns (codes uint8, descale float) with x ~= descale * value(codes)."""
+    amax = float(np.abs(x).max(initial=0.0))
+    descale = np.float32(amax / E4M3_MAX) if amax > 0 else np.float32(1.0)
+    while amax / float(descale) > E4M3_MAX:
+        descale = np.nextafter(descale, np.float32(np.inf))
+    return f32_to_e4m3_bits((x.astype(np.float64) / float(descale)).astype(np.float32)), float(descale)
+
+
+def make_inputs_fp8(B: int, H: int, S: int, D: int, seed: int, stress: bool = False) -> dict:
+    """Q, K, V drawn exactly as make_inputs (fp32, before any rounding), then
+    each quantized to E4M3 with its own per-tensor descale factor:
+    {"q", "k", "v": uint8 codes [B,H,S,D], "q_descale", "k_descale", "v_descale"}.
+    The exact values are descale * e4m3_bits_to_f64(codes)."""
+    rng = np.random.default_rng(seed)
+    shape = (B, H, S, D)
+    q = rng.standard_normal(shape, dtype=np.float32)
+    k = rng.standard_normal(shape, dtype=np.float32)
+    v = rng.standard_normal(shape, dtype=np.float32)
+    if stress:
+        q *= np.float32(3.0)
+        k *= np.float32(3.0)
+        q[..., 0] = np.float32(4.0)
+        k[..., 0] += (np.float32(0.002) * np.arange(S, dtype=np.float32))[None, None, :]
+    out = {}
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        out[name], out[name + "_descale"] = quantize_e4m3(t)
+    return out
+
+
+def fp8_dequantized(bits: dict) -> dict:
+    """fp64 values of an FP8 input set (exact: 4-bit significands times an
+    fp32 descale)."""
+    return {n: e4m3_bits_to_f64(bits[n]) * bits[n + "_descale"] for n in ("q", "k", "v")}
+
+
+def to_torch_u8(codes: np.ndarray, device=None):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8))
+    return t.to(device) if device is not None else t
 
 
 def workload_inputs(w: Workload) -> dict:

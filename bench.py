@@ -33,6 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
+PEAK_FP8_TFLOPS = 5033.2    # MI355X dense FP8 MFMA: twice the bf16 rate
 PEAK_HBM_GBS = 8000.0
 
 # HBM bytes per launch of the dominant kernel (the backward's dK/dV kernel on
@@ -419,6 +420,30 @@ def main():
                 log("  rescale events %s: %s" % (name, ev))
             del lq, lk, lv, lo, ll
             torch.cuda.empty_cache()
+        # The FP8 (E4M3) forward on the causal S=8192 shape (the same draws as
+        # the bf16 leg, quantized per tensor), against the FP8 dense peak.
+        fw = ai.FP8_WORKLOAD
+        b8 = ai.make_inputs_fp8(fw.B, fw.H, fw.S, fw.D, fw.seed)
+        q8, k8, v8 = (ai.to_torch_u8(b8[n], dev) for n in ("q", "k", "v"))
+        o8 = torch.empty(q8.shape, dtype=torch.bfloat16, device=dev)
+        l8 = torch.empty((fw.B, fw.H, fw.S), dtype=torch.float32, device=dev)
+        run8 = lambda: A.fwd_fp8_out(q8, k8, v8, b8["q_descale"], b8["k_descale"],
+                                     b8["v_descale"], o8, l8, causal=fw.causal, scale=fw.scale)
+        for _ in range(3):
+            run8()
+        ms = time_launches(run8, n_rep)
+        med = last_median()
+        fl = fwd_flops(fw.B, fw.H, fw.S, fw.D, fw.causal)
+        tf = fl / (ms * 1e-3) / 1e12
+        legs[fw.name] = {"shape": [fw.B, fw.H, fw.S, fw.D], "causal": fw.causal, "dtype": "e4m3",
+                         "ms": round(ms, 4), "median_ms": round(med, 4), "tflops": round(tf, 2),
+                         "frac_peak_fp8": round(tf / PEAK_FP8_TFLOPS, 4),
+                         "frac_peak_bf16": round(tf / PEAK_BF16_TFLOPS, 4),
+                         "speedup_vs_bf16": round(legs["fwd_causal_s8k"]["ms"] / ms, 3)}
+        log("fwd leg %s: %.4f ms  %.1f TFLOPS (%.1f%% of the FP8 peak, %.2fx the bf16 leg)" % (
+            fw.name, ms, tf, 100 * tf / PEAK_FP8_TFLOPS, legs[fw.name]["speedup_vs_bf16"]))
+        del q8, k8, v8, o8, l8
+        torch.cuda.empty_cache()
         # Context for the MFMA peak on this part: a plain vendor-library bf16 GEMM
         # (hipBLASLt through torch.matmul, contiguous 8192^3 operands, fp32
         # accumulate) timed the same way.  Not part of the attention path.

@@ -19,7 +19,8 @@ from . import _lib
 from ._lib import AttnError, load, library_path  # noqa: F401
 
 __all__ = ["fwd", "bwd", "fwd_out", "fwd_rescale_events", "bwd_out", "bwd_workspace_size",
-           "bwd_noalloc_out", "default_policy", "AttnError", "load", "library_path"]
+           "bwd_noalloc_out", "default_policy", "fwd_fp8", "fwd_fp8_out", "AttnError", "load",
+           "library_path"]
 
 
 def _check(t, name, shape=None, device=None):
@@ -99,6 +100,57 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None,
     lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
     fwd_out(q, k, v, o, lse, causal=causal, scale=scale, rescale_log2=rescale_log2,
             exp_poly_every=exp_poly_every)
+    return o, lse
+
+
+def _check_u8(t, name, shape=None, device=None):
+    """E4M3 codes: uint8, contiguous, 4-D, on q's GPU."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.dtype != torch.uint8:
+        raise TypeError("%s must hold E4M3 codes as torch.uint8, got %s" % (name, t.dtype))
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on a GPU device" % name)
+    if device is not None and t.device != device:
+        raise ValueError("%s is on %s, q on %s" % (name, t.device, device))
+    if not t.is_contiguous() or t.dim() != 4:
+        raise ValueError("%s must be contiguous 4-D [B,H,S,D]" % name)
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s shape %s != %s" % (name, tuple(t.shape), tuple(shape)))
+
+
+def fwd_fp8_out(q, k, v, q_descale, k_descale, v_descale, o, lse, causal: bool = False,
+                scale: float | None = None) -> None:
+    """FP8 forward (attn_fwd_fp8) into caller-provided o (bf16) and lse (fp32);
+    q, k, v are E4M3 codes (uint8 [B,H,S,D]) with one descale factor each."""
+    import torch
+    _check_u8(q, "q")
+    B, H, S, D = q.shape
+    _check_u8(k, "k", q.shape, q.device)
+    _check_u8(v, "v", q.shape, q.device)
+    if o.dtype != torch.bfloat16 or o.device != q.device or not o.is_contiguous() or \
+            tuple(o.shape) != tuple(q.shape):
+        raise ValueError("o must be contiguous bf16 [B,H,S,D] on q's device")
+    _check_lse(lse, B, H, S, q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    rc = _lib.load().attn_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                  lse.data_ptr(), B, H, S, D, float(scale), int(bool(causal)),
+                                  float(q_descale), float(k_descale), float(v_descale),
+                                  _stream(q.device))
+    _lib.raise_for(rc, "attn_fwd_fp8")
+
+
+def fwd_fp8(q, k, v, q_descale, k_descale, v_descale, causal: bool = False,
+            scale: float | None = None):
+    """Returns (O bf16 [B,H,S,D], LSE fp32 [B,H,S]) of the FP8 forward."""
+    import torch
+    _check_u8(q, "q")
+    B, H, S, D = q.shape
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    fwd_fp8_out(q, k, v, q_descale, k_descale, v_descale, o, lse, causal=causal, scale=scale)
     return o, lse
 
 

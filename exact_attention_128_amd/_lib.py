@@ -20,6 +20,7 @@ SIGNATURES = {
     "attn_fwd_ex": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _f, _vp]),
     "attn_fwd_policy": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _f, _i, _vp]),
     "attn_fwd_default_policy": (_i, [_i, _i, _i, ctypes.POINTER(_f), ctypes.POINTER(_i)]),
+    "attn_fwd_fp8": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _f, _f, _f, _vp]),
     "attn_fwd_rescale_events": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _f, _vp,
                                      _vp]),
     "attn_bwd_workspace_size": (_sz, [_i, _i, _i, _i]),

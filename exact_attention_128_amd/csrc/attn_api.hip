@@ -170,6 +170,37 @@ int attn_fwd_default_policy(int D, int causal, int S, float* rescale_log2, int* 
   return ATTN_OK;
 }
 
+int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                 int S, int D, float scale, int causal, float q_descale, float k_descale,
+                 float v_descale, attn_stream_t stream) {
+  if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
+  int rc = check_shape(B, H, S, D);
+  if (rc) return rc;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(lse, 4))
+    return ATTN_ERR_ALIGN;
+  for (float d : {q_descale, k_descale, v_descale})
+    if (!(isfinite(d) && d > 0.0f)) return ATTN_ERR_SCALE;
+  const float sc = scale * q_descale * k_descale;
+  if (!scale_ok(scale) || !scale_ok(sc)) return ATTN_ERR_SCALE;
+  attn::Fp8FwdParams p{};
+  p.q = static_cast<const uint8_t*>(q);
+  p.k = static_cast<const uint8_t*>(k);
+  p.v = static_cast<const uint8_t*>(v);
+  p.o = static_cast<uint16_t*>(o);
+  p.lse = lse;
+  p.bh = B * H;
+  p.S = S;
+  // as the bf16 forward: a negative scale negates the Q codes (sign bit of
+  // every byte), a zero scale zeroes them
+  p.qxor = sc < 0.0f ? 0x80808080u : 0u;
+  p.qand = sc == 0.0f ? 0u : 0xffffffffu;
+  p.c = sc == 0.0f ? 1.0f : fabsf(sc) * attn::kLog2eHost;
+  p.vscale = v_descale;
+  return attn::hip_status(attn::launch_fwd_fp8(p, D, causal != 0,
+                                               reinterpret_cast<hipStream_t>(stream)));
+}
+
 int attn_fwd_rescale_events(const void* q, const void* k, const void* v, void* o, float* lse,
                             int B, int H, int S, int D, float scale, int causal,
                             float rescale_log2, unsigned long long* events,

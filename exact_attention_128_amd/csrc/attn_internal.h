@@ -28,6 +28,25 @@ struct FwdParams {
   unsigned long long* events;  // diagnostic counters (see attn_fwd_rescale_events), or null
 };
 
+// One FP8 forward launch.  Q, K, V are [B*H][S][D] E4M3 codes (one byte per
+// element); the scores are (Q codes . K codes) * c with c = |scale * q_descale
+// * k_descale| * log2(e); O is bf16 and carries v_descale.
+struct Fp8FwdParams {
+  const uint8_t* q;
+  const uint8_t* k;
+  const uint8_t* v;
+  uint16_t* o;
+  float* lse;
+  int bh;
+  int S;
+  int nqb;
+  float c;        // > 0
+  float vscale;   // v_descale, applied to O
+  uint32_t qxor;  // 0, or 0x80808080 when scale < 0
+  uint32_t qand;  // 0xffffffff, or 0 when scale == 0
+  int xcd_heads;
+};
+
 // One backward launch.
 struct BwdParams {
   const uint16_t* q;
@@ -77,6 +96,8 @@ hipError_t launch_bwd(const BwdParams& p, int D, bool causal, unsigned phases, h
 // -- and slower at 256 keys, where the one-pass kernel's 128 KiB of LDS and
 // one wave per SIMD leave the chip underused: 46 against 39 us.)
 constexpr int kShortMaxS = 128;
+
+hipError_t launch_fwd_fp8(const Fp8FwdParams& p, int D, bool causal, hipStream_t stream);
 hipError_t launch_fwd_short(const FwdParams& p, int D, bool causal, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdParams& p, int D, bool causal, hipStream_t stream);
 

@@ -148,6 +148,34 @@ int attn_fwd_policy(const void* q, const void* k, const void* v, void* o, float*
 int attn_fwd_default_policy(int D, int causal, int S, float* rescale_log2, int* exp_poly_every);
 
 /*
+ * FP8 forward: the same O and LSE for Q, K, V given as OCP FP8 E4M3 codes
+ * (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; 0x7f/0xff NaN,
+ * largest finite 448) with one descale factor per tensor: the inputs are
+ * Q = q_descale * value(q codes), and likewise K and V.  The precision lever
+ * of the Tencent Cloud article, section 5, on the gfx950 FP8 matrix core:
+ * both products run in E4M3 with fp32 accumulation.
+ *   q, k, v    [B][H][S][D] E4M3 codes (one byte each), 16-byte aligned.
+ *   o          [B][H][S][D] bf16, written (v_descale applied).
+ *   lse        [B][H][S] fp32, written (natural log, as attn_fwd).
+ *   q_descale, k_descale, v_descale   finite and > 0.
+ * Arithmetic: the score products are exact (E4M3 x E4M3 fits fp32) and summed
+ * in fp32; the softmax weights are rounded to E4M3 (to nearest even, relative
+ * error <= 2^-4, weights under 2^-10 of a row's largest times 4 flushed to
+ * zero) before the PV product, and O is normalised by the sum of exactly those
+ * rounded weights, so each output row is a convex combination of V rows; the
+ * LSE takes the fp32 sum of the unrounded weights.  Every row's O therefore
+ * sits within (2^-4 / (1 - 2^-4)) * sum_j P_ij |V_j - O_i| (plus the flushed
+ * weights' share and the bf16 output rounding) of the exact result on the
+ * dequantized inputs; the LSE within the bf16 path's bound.  Sequences of
+ * any length take the same kernel.  Errors as attn_fwd; a descale factor not
+ * finite and positive, or scale * q_descale * k_descale * log2(e) not finite:
+ * ATTN_ERR_SCALE.
+ */
+int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int H, int S, int D, float scale, int causal, float q_descale,
+                 float k_descale, float v_descale, attn_stream_t stream);
+
+/*
  * Diagnostic forward that also counts the conditional-rescale events (the FA4
  * technique of rescaling only when the maximum threatens the number range,
  * Tencent Cloud article, section 7).  The kernel tests once per wave (32

@@ -134,3 +134,106 @@ def assert_grads_ok(err, what=""):
     for n, e in err.items():
         assert np.isfinite(e) and e <= GRAD_MAX, "%s %s max err %.3e > %.1e (%s)" % (
             what, n, e, GRAD_MAX, err)
+
+
+# ---- FP8 forward: the bound of its accuracy contract (E4M3 weights).
+#
+# The kernel rounds each softmax weight (offset so that a row's largest weight
+# in the first tile is 4) to E4M3 before the PV product and normalises by the
+# sum of the rounded weights, so O is a convex combination of V rows with
+# perturbed weights.  With e_j = 4 exp(s_j - max s) (the frame in which the
+# row's largest weight is exactly 4; the kernel's stale-maximum frame only
+# scales all weights up, which can only shrink the relative rounding error),
+# each rounded weight is within d_j = 2^-4 e_j + min(e_j, 2^-10) of e_j (half an
+# ulp relative for normal E4M3 values, half the subnormal spacing 2^-9
+# absolute below them, and flushed-to-zero weights losing at most themselves),
+# hence per element
+#   |O_i - O_ref_i| <= sum_j d_j |V_j - O_ref_i| / (sum_j e_j - sum_j d_j)
+# plus the bf16 output rounding (2^-9 relative, taken as 2^-8 for the fp32
+# normalisation) and the fp32 accumulation over up to 2^13 keys (1e-3 max|V|).
+#
+# The scores themselves carry the FP8 matrix core's accumulation error: it
+# does not add its 64 exact products in full fp32 (measured on gfx950:
+# |err| <= 2^-11.6 sum_k |a_k b_k| with widely mixed magnitudes, 2^-14.7 for
+# N(0,1) operands), so each score is within FP8_EPS * A_ij of exact, with
+# A_ij = |scale| sum_d |Q_id K_jd| and FP8_EPS = 2^-10 (a margin of 3 over the
+# worst measured).  A weight is then perturbed by a factor within
+# exp(+-FP8_EPS A_ij) before its E4M3 rounding, and the LSE (a smooth maximum
+# of the scores) by at most max_j FP8_EPS A_ij on top of the fp32 bound 1e-3.
+FP8_U = 2.0 ** -4
+FP8_FLUSH = 2.0 ** -10
+FP8_EPS = 2.0 ** -10
+
+
+def fp8_row_bounds(q, k, v, scale, causal, rows, o_ref, with_lse=False):
+    """Per-element bounds [n, D] for query rows `rows` of one head (fp64
+    inputs [S, D], o_ref the oracle's O for those rows [n, D]); with
+    with_lse, also the per-row LSE bounds [n]."""
+    S = k.shape[0]
+    out = np.empty_like(o_ref)
+    lse_b = np.empty(len(rows))
+    ak = np.abs(k)
+    for n, i in enumerate(rows):
+        nv = i + 1 if causal else S
+        s = scale * (k[:nv] @ q[i])
+        a = abs(scale) * (ak[:nv] @ np.abs(q[i]))
+        e = 4.0 * np.exp(s - s.max())
+        d = ((1.0 + FP8_U) * np.exp(FP8_EPS * a) - 1.0) * e + np.minimum(e, FP8_FLUSH)
+        dev = np.abs(v[:nv] - o_ref[n][None, :])
+        out[n] = (d @ dev) / (e.sum() - d.sum()) + 2.0 ** -8 * np.abs(o_ref[n]) + \
+            1e-3 * np.abs(v[:nv]).max()
+        lse_b[n] = LSE_MAX + FP8_EPS * a.max()
+    return (out, lse_b) if with_lse else out
+
+
+def gpu_fwd_fp8(bits, causal, scale):
+    """FP8 forward on cuda:0; returns (O fp64, LSE fp64)."""
+    import torch
+    import exact_attention_128_amd as A
+    dev = torch.device("cuda", 0)
+    q, k, v = (ai.to_torch_u8(bits[n], dev) for n in ("q", "k", "v"))
+    o, lse = A.fwd_fp8(q, k, v, bits["q_descale"], bits["k_descale"], bits["v_descale"],
+                       causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return (ai.bf16_bits_to_f64(ai.torch_bf16_to_bits(o)),
+            lse.cpu().numpy().astype(np.float64))
+
+
+def check_fp8(bits, causal, scale, rows_by_head=None, what=""):
+    """FP8 forward against the oracle on the dequantized inputs: every element
+    (or the sampled rows) within its bound, LSE within LSE_MAX.  Returns the
+    error statistics."""
+    B, H, S, D = bits["q"].shape
+    o, lse = gpu_fwd_fp8(bits, causal, scale)
+    deq = ai.fp8_dequantized(bits)
+    qd, kd, vd = (deq[n].reshape(B * H, S, D) for n in ("q", "k", "v"))
+    o = o.reshape(B * H, S, D)
+    lse = lse.reshape(B * H, S)
+    if rows_by_head is None:
+        o_ref, lse_ref = oracle.attn_fwd(deq["q"], deq["k"], deq["v"], scale, causal)
+        o_ref, lse_ref = o_ref.reshape(B * H, S, D), lse_ref.reshape(B * H, S)
+        rows_by_head = {hd: np.arange(S) for hd in range(B * H)}
+        ref = {hd: (o_ref[hd], lse_ref[hd]) for hd in rows_by_head}
+    else:
+        ref = {hd: oracle.attn_fwd_rows(qd[hd, rows], rows, kd[hd], vd[hd], scale, causal)
+               for hd, rows in rows_by_head.items()}
+    worst, errs, lerr, lworst = 0.0, [], 0.0, 0.0
+    for hd, rows in rows_by_head.items():
+        r_o, r_l = ref[hd]
+        got = o[hd, rows]
+        bound, lbound = fp8_row_bounds(qd[hd], kd[hd], vd[hd], scale, causal, rows, r_o,
+                                       with_lse=True)
+        err = np.abs(got - r_o)
+        assert np.all(np.isfinite(got)), "%s non-finite O" % what
+        worst = max(worst, float((err / bound).max()))
+        errs.append(err)
+        le = np.abs(lse[hd, rows] - r_l)
+        lerr = max(lerr, float(le.max()))
+        lworst = max(lworst, float((le / lbound).max()))
+    err = np.concatenate([e.ravel() for e in errs])
+    stats = {"o_max": float(err.max()), "o_mean": float(err.mean()),
+             "max_err_over_bound": worst, "lse_max": lerr, "lse_err_over_bound": lworst}
+    print(what, stats)
+    assert worst <= 1.0, "%s O outside its bound: %s" % (what, stats)
+    assert lworst <= 1.0, "%s LSE outside its bound: %s" % (what, stats)
+    return stats
