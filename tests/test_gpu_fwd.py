@@ -78,6 +78,18 @@ def test_multi_block_lengths(D, causal):
     P.assert_fwd_ok(err, "S=1500 D=%d causal=%s" % (D, causal))
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [(3, 67, 600, 128), (1, 40, 3000, 128), (2, 9, 1111, 64)])
+def test_many_units(shape, causal):
+    """Grids of several workgroups per CU in both block orders: 201 heads of 3
+    query blocks (plain order, 603 workgroups), 40 heads of 12 blocks (XCD
+    order, 480 workgroups), 18 heads of 5 blocks at D = 64; every element
+    against the oracle."""
+    B, H, S, D = shape
+    err = _full_case(B, H, S, D, causal, seed=4000 + S + int(causal))
+    P.assert_fwd_ok(err, "persistent %s causal=%s" % (shape, causal))
+
+
 @pytest.mark.parametrize("scale", [1.0, -0.09, 0.0, 0.5, 16.0])
 def test_scale_values(scale):
     """Off-standard scales, up to 16 (scores of a few hundred, rows dominated by
