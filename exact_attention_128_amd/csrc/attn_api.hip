@@ -38,9 +38,10 @@ int check_shape(int B, int H, int S, int D) {
   if (D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
   const int64_t bh = int64_t(B) * H;
   if (bh > 0x7fffffffLL) return ATTN_ERR_SHAPE;
-  if (bh * S * D >= kMaxElems) return ATTN_ERR_SHAPE;
-  // the kernels address one head's [S][D] bf16 slab with 32-bit byte offsets
+  // the kernels address one head's [S][D] bf16 slab with 32-bit byte offsets;
+  // checked first, it also keeps the element count below 2^31 * 2^29
   if (int64_t(S) * D >= (int64_t(1) << 29)) return ATTN_ERR_SHAPE;
+  if (bh * (int64_t(S) * D) >= kMaxElems) return ATTN_ERR_SHAPE;
   if (bh * ((int64_t(S) + 255) / 256) >= kMaxRowBlocks) return ATTN_ERR_SHAPE;
   return ATTN_OK;
 }
@@ -220,9 +221,9 @@ int attn_bwd_phases(const void* q, const void* k, const void* v, const void* o,
                     const float* lse, const void* dout, void* dq, void* dk, void* dv,
                     void* workspace, size_t workspace_bytes, int B, int H, int S, int D,
                     float scale, int causal, unsigned phases, attn_stream_t stream) {
+  if (!workspace) return ATTN_ERR_NULL;   // null pointers first, as every entry point
   int rc = attn::check_bwd_args(q, k, v, o, lse, dout, dq, dk, dv, B, H, S, D, scale);
   if (rc) return rc;
-  if (!workspace) return ATTN_ERR_NULL;
   if (!aligned(workspace, 256)) return ATTN_ERR_ALIGN;
   if (workspace_bytes < attn_bwd_workspace_size(B, H, S, D)) return ATTN_ERR_WORKSPACE;
 
