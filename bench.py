@@ -45,15 +45,16 @@ TRAFFIC_SOURCES = ("exact_attention_128_amd/csrc/attn_bwd.hip",
                    "exact_attention_128_amd/csrc/gfx950.h",
                    "exact_attention_128_amd/csrc/attn_internal.h",
                    "exact_attention_128_amd/build.py")
-TRAFFIC = {"workload": "bwd_causal_s4k", "read_bytes": 229614928, "write_bytes": 67108864,
-           "sources_sha256": "66e0a4429efccac5dbb6ea76b8eacd3bc9f34ee3f7fdb1a7643a40a8e531a731"}
+TRAFFIC = {"workload": "bwd_causal_s4k", "read_bytes": 224928572, "write_bytes": 67108864,
+           "sources_sha256": "07c2b146a8577265a693c26a1825807faa0a3731f28ee9ad053f07e5d847337b"}
 # the same for the forward on the causal S=8192 workload
 # (profiles/fwd_causal_s8k_counters.md)
 FWD_TRAFFIC_SOURCES = ("exact_attention_128_amd/csrc/attn_fwd.hip",
                        "exact_attention_128_amd/csrc/gfx950.h",
-                       "exact_attention_128_amd/csrc/attn_internal.h")
-FWD_TRAFFIC = {"workload": "fwd_causal_s8k", "read_bytes": 1383277078, "write_bytes": 136327957,
-               "sources_sha256": "0e362226999274409113f2846a76f04db26a54173f82e95b4e8da58710f2179c"}
+                       "exact_attention_128_amd/csrc/attn_internal.h",
+                       "exact_attention_128_amd/build.py")
+FWD_TRAFFIC = {"workload": "fwd_causal_s8k", "read_bytes": 1388079682, "write_bytes": 136322645,
+               "sources_sha256": "487266126d82623c9e07cf5c24d0a9cbe48ef959f837bc3892eba838e2125165"}
 
 
 def measured_traffic(workload, record=None, sources=None):
@@ -121,6 +122,8 @@ def _grids(w):
     g = {"attn_bwd_dq_kernel": bh * (-(-S // 256)) * 512,
          "attn_bwd_main_kernel": bh * (-(-S // 128)) * 256,
          "attn_bwd_pre_kernel": min(-(-(bh * (-(-S // 64)) * 64 * (D // 8)) // 256), 1024) * 256}
+    if w.name.endswith("_fp8"):
+        return {"attn_fwd_fp8_kernel": bh * (-(-S // 256)) * 512}
     if S <= 128:
         g["attn_fwd_short_kernel"] = bh * 256
     else:
@@ -131,6 +134,7 @@ def _grids(w):
 # share of a workload's algorithmic flops credited to each kernel (the dK/dV
 # kernel does four of the backward's five products, the dQ kernel the fifth)
 _CREDIT = {"attn_fwd_kernel": ("fwd", 1.0), "attn_fwd_short_kernel": ("fwd", 1.0),
+           "attn_fwd_fp8_kernel": ("fwd", 1.0),
            "attn_bwd_main_kernel": ("bwd", 0.8), "attn_bwd_dq_kernel": ("bwd", 0.2)}
 
 
@@ -139,7 +143,8 @@ def trace_summary(path):
     --output-format csv): one row per (kernel, grid size), named by the
     workload whose launch has that grid, with mean / median / min / max
     duration and, for the attention kernels, the algorithmic rate and the
-    fraction of the dense bf16 peak computed from the trace's mean."""
+    fraction of the dense peak of the kernel's input type (bf16, or FP8 for
+    the E4M3 forward) computed from the trace's mean."""
     import csv
     import statistics
     import attn_inputs as ai
@@ -151,13 +156,13 @@ def trace_summary(path):
             rows.setdefault((name, int(r["Grid_Size_X"])), []).append(dur)
     total = sum(sum(v) for v in rows.values())
     out = ["| Kernel | Workload | Grid (work-items) | Calls | Mean (us) | Median (us) | Min (us) "
-           "| Max (us) | Share | Algorithmic TFLOPS (mean) | Fraction of 2516.6 |",
+           "| Max (us) | Share | Algorithmic TFLOPS (mean) | Fraction of dense peak |",
            "|---|---|---|---|---|---|---|---|---|---|---|"]
     for (name, grid), d in sorted(rows.items(), key=lambda kv: -sum(kv[1])):
         fam = name.split("<")[0].split("::")[-1].strip()
         targs = name.split("<")[1].split(">")[0].split(",") if "<" in name else []
         wl, tf, frac = "", "", ""
-        for w in ai.WORKLOADS.values():
+        for w in list(ai.WORKLOADS.values()) + [ai.FP8_WORKLOAD]:
             if fam.startswith("attn_") and targs and int(targs[0]) == w.D and \
                     (len(targs) < 2 or targs[1].strip() == ("true" if w.causal else "false")) and \
                     _grids(w).get(fam) == grid and (fam.startswith("attn_fwd") or w.backward):
@@ -166,13 +171,138 @@ def trace_summary(path):
                     kind, share = _CREDIT[fam]
                     f = fwd_flops(w.B, w.H, w.S, w.D, w.causal) * (2.5 if kind == "bwd" else 1.0)
                     t = share * f / (statistics.mean(d) * 1e-6) / 1e12
-                    tf, frac = "%.1f" % t, "%.4f" % (t / PEAK_BF16_TFLOPS)
+                    peak = PEAK_FP8_TFLOPS if fam == "attn_fwd_fp8_kernel" else PEAK_BF16_TFLOPS
+                    tf, frac = "%.1f" % t, "%.4f of %.1f" % (t / peak, peak)
                 break
         shown = name if len(name) <= 100 else name[:60] + " ... (library kernel)"
         out.append("| `%s` | %s | %d | %d | %.1f | %.1f | %.1f | %.1f | %.1f%% | %s | %s |" % (
             shown, wl or "-", grid, len(d), statistics.mean(d), statistics.median(d), min(d),
             max(d), 100.0 * sum(d) / total, tf, frac))
     return "\n".join(out)
+
+
+# Counter sets of the hardware-counter profiles, one rocprofv3 run each (one
+# run holds at most 8 SQ_, 4 TCC_ and 2 GRBM_ counters); passes 3 and 4 are the
+# HBM byte counters, also taken for the calibrating copy.
+PMC_PASSES = {
+    1: "SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA SQ_INSTS_LDS "
+       "SQ_LDS_BANK_CONFLICT SQ_WAIT_INST_LDS GRBM_GUI_ACTIVE",
+    2: "SQ_INSTS_VALU SQ_INSTS_VALU_TRANS_F32 SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_ANY SQ_WAIT_ANY "
+       "SQ_WAIT_INST_ANY SQ_INSTS_SALU GRBM_GUI_ACTIVE",
+    3: "FETCH_SIZE",
+    4: "WRITE_SIZE",
+    5: "SQ_LDS_IDX_ACTIVE SQ_LDS_CMD_FIFO_FULL SQ_VALU_MFMA_COEXEC_CYCLES SQ_ACTIVE_INST_LDS "
+       "SQ_ACTIVE_INST_SCA SQ_ACTIVE_INST_VMEM SQ_ACTIVE_INST_MISC GRBM_GUI_ACTIVE",
+}
+
+
+def pmc_command(n, workload, outdir="gpurun_out/pmc"):
+    """The rocprofv3 command of counter pass n over one workload (run from the
+    repository root)."""
+    return ("rocprofv3 --pmc %s --output-format csv -d %s/p%d_%s -o run -- "
+            "python3 bench.py --only %s --steps 2 --warmup 1" % (PMC_PASSES[n], outdir, n,
+                                                                  workload, workload))
+
+
+def _pmc_load(path):
+    """{kernel name: {counter: mean per-dispatch value}} of one counter CSV."""
+    import csv
+    per = {}
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            per.setdefault(r["Kernel_Name"], {}).setdefault(r["Counter_Name"], []).append(
+                float(r["Counter_Value"]))
+    return {k: {c: sum(v) / len(v) for c, v in d.items()} for k, d in per.items()}
+
+
+def _alg_bytes(fam, w):
+    """(read, write) algorithmic HBM bytes of one launch of kernel family fam
+    on workload w: each input read once and each output written once (bf16
+    tensors, E4M3 codes for the FP8 forward's inputs, fp32 LSE and the
+    backward's per-64-row statistics)."""
+    T = w.B * w.H * w.S * w.D * 2
+    L = w.B * w.H * w.S * 4
+    ST = w.B * w.H * (-(-w.S // 64)) * 512
+    return {"attn_fwd_kernel": (3 * T, T + L), "attn_fwd_short_kernel": (3 * T, T + L),
+            "attn_fwd_fp8_kernel": (3 * T // 2, T + L),
+            "attn_bwd_dq_kernel": (5 * T + L, T + ST), "attn_bwd_main_kernel": (4 * T + ST, 2 * T),
+            "attn_bwd_pre_kernel": (2 * T + L, ST)}.get(fam, (None, None))
+
+
+def pmc_summary(root, workload):
+    """Markdown summary of the five counter passes of one workload, read from
+    <root>/p<n>_<workload>/run_counter_collection.csv, with the HBM byte
+    counters scaled by what they read for the 1 GiB calibrating copy
+    (<root>/p3_copy, <root>/p4_copy).  Prints per kernel the derived shares,
+    the instruction counts, the measured and algorithmic HBM bytes, and every
+    raw counter."""
+    import os.path as op
+    import attn_inputs as ai
+    w = ai.FP8_WORKLOAD if workload == ai.FP8_WORKLOAD.name else ai.WORKLOADS[workload]
+    csvf = lambda n, wl: op.join(root, "p%d_%s" % (n, wl), "run_counter_collection.csv")
+    copy_kernel = lambda d: next(v for k, v in d.items() if "copyBuffer" in k)
+    cf = copy_kernel(_pmc_load(csvf(3, "copy")))["FETCH_SIZE"]
+    cw = copy_kernel(_pmc_load(csvf(4, "copy")))["WRITE_SIZE"]
+    fs, ws = 1048576.0 / cf, 1048576.0 / cw
+    raw = {}
+    for n in PMC_PASSES:
+        for k, d in _pmc_load(csvf(n, workload)).items():
+            raw.setdefault(k, {}).update(d)
+    short = lambda k: k.replace("void ", "").split("(")[0]
+    fam = lambda k: short(k).split("<")[0].split("::")[-1]
+    kind = "backward after one forward" if w.backward else "forward"
+    o = ["# Hardware counters: %s B=%d H=%d S=%d D=%d%s (%s)\n" % (
+        workload, w.B, w.H, w.S, w.D, " causal" if w.causal else "", kind),
+        "Collected on one MI355X, each counter set in its own run, from the repository root "
+        "(the profiler wants `cd /tmp && export TMPDIR=/tmp` first and then absolute paths "
+        "to the same files), then summarised by the last command:\n", "```"]
+    o += [pmc_command(n, workload) for n in PMC_PASSES]
+    o += [pmc_command(n, "copy") for n in (3, 4)]
+    o += ["python3 bench.py --pmc-summary gpurun_out/pmc %s" % workload, "```\n"]
+    o.append("""Values are per dispatch, averaged over the run's dispatches of each kernel.  Derived columns:
+- MFMA busy = `SQ_VALU_MFMA_BUSY_CYCLES` / (`GRBM_GUI_ACTIVE` / 8 XCDs x 1024 SIMDs): the share of the
+  kernel's wall cycles (at the clock it ran at) in which the matrix cores were busy.
+- LDS busy = `SQ_LDS_IDX_ACTIVE` / (`GRBM_GUI_ACTIVE` / 8 x 256 CUs).  Co-exec =
+  `SQ_VALU_MFMA_COEXEC_CYCLES` / `SQ_VALU_MFMA_BUSY_CYCLES`.
+- Wave time shares (`SQ_*` / `SQ_WAVE_CYCLES`): issuing (`SQ_ACTIVE_INST_ANY`), blocked on issue
+  (`SQ_WAIT_INST_ANY`), waiting in `s_waitcnt` or at a barrier (`SQ_WAIT_ANY`).
+- HBM bytes: `FETCH_SIZE` and `WRITE_SIZE` (KiB) scaled by what the same counters read for a plain
+  1 GiB device copy (`bench.py --only copy`), which reads FETCH_SIZE %d KiB and WRITE_SIZE %d KiB for
+  1 048 576 KiB moved: FETCH_SIZE is multiplied by %.3f, WRITE_SIZE by %.3f.  Algorithmic bytes: each
+  input read once and each output written once.
+""" % (round(cf), round(cw), fs, ws))
+    o.append("| Kernel | cycles per XCD | MFMA busy | LDS busy | co-exec | issuing / blocked / "
+             "waiting | MFMA instr | VALU instr | transcendental share | LDS instr | bank conflicts "
+             "| HBM read (MB) | alg. read (MB) | HBM write (MB) | alg. write (MB) |")
+    o.append("|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|")
+    order = sorted(raw, key=lambda k: ("pre" in k, "main" in k, "dq" in k, k))
+    for k in order:
+        d = raw[k]
+        cyc = d["GRBM_GUI_ACTIVE"] / 8
+        ar, aw = _alg_bytes(fam(k), w)
+        mb = lambda x: "-" if x is None else "%.1f" % (x / 1e6)
+        o.append("| `%s` | %d | %.1f%% | %.1f%% | %.1f%% | %d%% / %d%% / %d%% | %d | %d | %.1f%% "
+                 "| %d | %d | %.1f | %s | %.1f | %s |" % (
+                     short(k), round(cyc), 100 * d["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * 1024),
+                     100 * d["SQ_LDS_IDX_ACTIVE"] / (cyc * 256),
+                     100 * d["SQ_VALU_MFMA_COEXEC_CYCLES"] / max(1.0, d["SQ_VALU_MFMA_BUSY_CYCLES"]),
+                     round(100 * d["SQ_ACTIVE_INST_ANY"] / d["SQ_WAVE_CYCLES"]),
+                     round(100 * d["SQ_WAIT_INST_ANY"] / d["SQ_WAVE_CYCLES"]),
+                     round(100 * d["SQ_WAIT_ANY"] / d["SQ_WAVE_CYCLES"]),
+                     d["SQ_INSTS_MFMA"], d["SQ_INSTS_VALU"],
+                     100 * d["SQ_INSTS_VALU_TRANS_F32"] / max(1.0, d["SQ_INSTS_VALU"]),
+                     d["SQ_INSTS_LDS"], d["SQ_LDS_BANK_CONFLICT"],
+                     d["FETCH_SIZE"] * 1024 * fs / 1e6, mb(ar), d["WRITE_SIZE"] * 1024 * ws / 1e6,
+                     mb(aw)))
+    o.append("\nHBM bytes per launch (scaled): " + "; ".join(
+        "`%s` read %d, write %d" % (fam(k), round(raw[k]["FETCH_SIZE"] * 1024 * fs),
+                                    round(raw[k]["WRITE_SIZE"] * 1024 * ws)) for k in order) + "\n")
+    o += ["Raw per-dispatch averages:\n", "| Kernel | Counter | Value |", "|---|---|---|"]
+    for k in order:
+        for c in sorted(raw[k]):
+            v = raw[k][c]
+            o.append("| `%s` | %s | %s |" % (short(k), c, ("%.1f" % v) if v != int(v) else "%d" % v))
+    return "\n".join(o)
 
 
 SWEEP_TAUS = (0.0, 8.0, 16.0, 32.0, 64.0)
@@ -257,6 +387,9 @@ def main():
     ap.add_argument("--trace-summary", default=None, metavar="KERNEL_TRACE_CSV",
                     help="print a per-workload markdown summary of a rocprofv3 kernel-trace "
                          "CSV and exit (no GPU needed)")
+    ap.add_argument("--pmc-summary", nargs=2, default=None, metavar=("PMC_DIR", "WORKLOAD"),
+                    help="print the markdown summary of one workload's counter passes "
+                         "(rocprofv3 --pmc CSVs under PMC_DIR) and exit (no GPU needed)")
     ap.add_argument("--sweep-policy", action="store_true",
                     help="time the forward at every (rescale threshold, exponential policy) "
                          "pair on the forward workloads and print the table (uses --steps, "
@@ -267,6 +400,9 @@ def main():
         return
     if args.trace_summary is not None:
         print(trace_summary(args.trace_summary))
+        return
+    if args.pmc_summary is not None:
+        print(pmc_summary(*args.pmc_summary))
         return
     if args.only is not None:
         run_only(args)
@@ -561,6 +697,18 @@ def run_only(args):
         torch.cuda.synchronize()
         print("ran copy: %d launches of a %d-byte device copy" % (args.warmup + args.steps, n),
               flush=True)
+        return
+    if args.only == ai.FP8_WORKLOAD.name:
+        w = ai.FP8_WORKLOAD
+        b8 = ai.make_inputs_fp8(w.B, w.H, w.S, w.D, w.seed)
+        q8, k8, v8 = (ai.to_torch_u8(b8[n], dev) for n in ("q", "k", "v"))
+        o8 = torch.empty(q8.shape, dtype=torch.bfloat16, device=dev)
+        l8 = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=dev)
+        for _ in range(args.warmup + args.steps):
+            A.fwd_fp8_out(q8, k8, v8, b8["q_descale"], b8["k_descale"], b8["v_descale"], o8, l8,
+                          causal=w.causal, scale=w.scale)
+        torch.cuda.synchronize()
+        print("ran %s: %d launches (FP8 forward)" % (w.name, args.warmup + args.steps), flush=True)
         return
     w = ai.WORKLOADS[args.only]
     bits = ai.make_inputs(w.B, w.H, w.S, w.D, w.seed, stress=w.stress, with_dout=w.backward)
