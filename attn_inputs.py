@@ -71,6 +71,20 @@ WORKLOADS = {
     "bwd_causal_s4k": Workload("bwd_causal_s4k", 2, 16, 4096, 128, True, backward=True, index=5),
 }
 
+# Many short heads: the memory-bound side of the forward's roofline (a few
+# flops per byte, so HBM throughput, not the matrix cores, bounds them).  Same
+# i.i.d. N(0,1) draws as the five workloads; 2^12 to 2^14 heads each.
+SHORT_WORKLOADS = {
+    "fwd_short_s128_h4096": Workload("fwd_short_s128_h4096", 64, 64, 128, 128, False, index=6),
+    "fwd_short_s64_d64_h8192": Workload("fwd_short_s64_d64_h8192", 128, 64, 64, 64, False,
+                                        index=7),
+    "fwd_short_s32_causal_h16384": Workload("fwd_short_s32_causal_h16384", 256, 64, 32, 128,
+                                            True, index=8),
+}
+
+# every named workload, by name
+ALL_WORKLOADS = {**WORKLOADS, **SHORT_WORKLOADS}
+
 # The FP8 forward measured on the causal long-sequence shape (same seed and
 # draws as fwd_causal_s8k, quantized to E4M3 per tensor).
 FP8_WORKLOAD = Workload("fwd_causal_s8k_fp8", 2, 32, 8192, 128, True, index=3)

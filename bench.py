@@ -125,7 +125,8 @@ def _grids(w):
     if w.name.endswith("_fp8"):
         return {"attn_fwd_fp8_kernel": bh * (-(-S // 256)) * 512}
     if S <= 128:
-        g["attn_fwd_short_kernel"] = bh * 256
+        hpw = 4 if S <= 32 else 2 if S <= 64 else 1   # heads per workgroup
+        g["attn_fwd_short_kernel"] = -(-bh // hpw) * 256
     else:
         g["attn_fwd_kernel"] = bh * (-(-S // 256)) * 512
     return g
@@ -156,28 +157,34 @@ def trace_summary(path):
             rows.setdefault((name, int(r["Grid_Size_X"])), []).append(dur)
     total = sum(sum(v) for v in rows.values())
     out = ["| Kernel | Workload | Grid (work-items) | Calls | Mean (us) | Median (us) | Min (us) "
-           "| Max (us) | Share | Algorithmic TFLOPS (mean) | Fraction of dense peak |",
-           "|---|---|---|---|---|---|---|---|---|---|---|"]
+           "| Max (us) | Share | Algorithmic TFLOPS (mean) | Fraction of dense peak "
+           "| Algorithmic HBM GB/s (mean, forward) |",
+           "|---|---|---|---|---|---|---|---|---|---|---|---|"]
     for (name, grid), d in sorted(rows.items(), key=lambda kv: -sum(kv[1])):
         fam = name.split("<")[0].split("::")[-1].strip()
         targs = name.split("<")[1].split(">")[0].split(",") if "<" in name else []
-        wl, tf, frac = "", "", ""
-        for w in list(ai.WORKLOADS.values()) + [ai.FP8_WORKLOAD]:
+        wl, tf, frac, gbs = "", "", "", ""
+        for w in list(ai.ALL_WORKLOADS.values()) + [ai.FP8_WORKLOAD]:
             if fam.startswith("attn_") and targs and int(targs[0]) == w.D and \
                     (len(targs) < 2 or targs[1].strip() == ("true" if w.causal else "false")) and \
                     _grids(w).get(fam) == grid and (fam.startswith("attn_fwd") or w.backward):
                 wl = w.name
-                if fam in _CREDIT and (len(targs) < 3 or targs[2].strip() in ("false", "2")):
+                if fam in _CREDIT and (len(targs) < 3 or targs[2].strip() != "true"):
                     kind, share = _CREDIT[fam]
                     f = fwd_flops(w.B, w.H, w.S, w.D, w.causal) * (2.5 if kind == "bwd" else 1.0)
                     t = share * f / (statistics.mean(d) * 1e-6) / 1e12
                     peak = PEAK_FP8_TFLOPS if fam == "attn_fwd_fp8_kernel" else PEAK_BF16_TFLOPS
                     tf, frac = "%.1f" % t, "%.4f of %.1f" % (t / peak, peak)
+                    if kind == "fwd":
+                        nb = 8.0 * w.B * w.H * w.S * w.D + 4.0 * w.B * w.H * w.S
+                        if fam == "attn_fwd_fp8_kernel":   # E4M3 inputs, bf16 O
+                            nb -= 3.0 * w.B * w.H * w.S * w.D
+                        gbs = "%.1f" % (nb / (statistics.mean(d) * 1e-6) / 1e9)
                 break
         shown = name if len(name) <= 100 else name[:60] + " ... (library kernel)"
-        out.append("| `%s` | %s | %d | %d | %.1f | %.1f | %.1f | %.1f | %.1f%% | %s | %s |" % (
+        out.append("| `%s` | %s | %d | %d | %.1f | %.1f | %.1f | %.1f | %.1f%% | %s | %s | %s |" % (
             shown, wl or "-", grid, len(d), statistics.mean(d), statistics.median(d), min(d),
-            max(d), 100.0 * sum(d) / total, tf, frac))
+            max(d), 100.0 * sum(d) / total, tf, frac, gbs))
     return "\n".join(out)
 
 
@@ -238,7 +245,7 @@ def pmc_summary(root, workload):
     raw counter."""
     import os.path as op
     import attn_inputs as ai
-    w = ai.FP8_WORKLOAD if workload == ai.FP8_WORKLOAD.name else ai.WORKLOADS[workload]
+    w = ai.FP8_WORKLOAD if workload == ai.FP8_WORKLOAD.name else ai.ALL_WORKLOADS[workload]
     csvf = lambda n, wl: op.join(root, "p%d_%s" % (n, wl), "run_counter_collection.csv")
     copy_kernel = lambda d: next(v for k, v in d.items() if "copyBuffer" in k)
     cf = copy_kernel(_pmc_load(csvf(3, "copy")))["FETCH_SIZE"]
@@ -516,8 +523,9 @@ def main():
     if not args.no_legs:
         del q, k, v, do, o, lse, dq, dk, dv, ws
         torch.cuda.empty_cache()
-        for name in ("tiny", "fwd_s2k", "fwd_causal_s8k", "fwd_stress_s16k"):
-            lw = ai.WORKLOADS[name]
+        for name in ("tiny", "fwd_s2k", "fwd_causal_s8k", "fwd_stress_s16k",
+                     *ai.SHORT_WORKLOADS):
+            lw = ai.ALL_WORKLOADS[name]
             lb = ai.workload_inputs(lw)
             lq, lk, lv = (ai.to_torch_bf16(lb[n], dev) for n in ("q", "k", "v"))
             lo = torch.empty_like(lq)
@@ -542,7 +550,7 @@ def main():
             if not args.no_cpu_baseline:
                 cpu_legs[name] = oracle_fwd_sample(lw, lb, args.cpu_leg_seconds)
                 log("  cpu oracle %s: %s" % (name, cpu_legs[name]))
-            if lw.causal:
+            if lw.causal and lw.S > 128:
                 # untimed: how often the conditional rescale fires (the counting
                 # forward, attn_fwd_rescale_events), at the library's threshold
                 # 2^64, at 2^32 and at FA4's 2^8
@@ -710,7 +718,7 @@ def run_only(args):
         torch.cuda.synchronize()
         print("ran %s: %d launches (FP8 forward)" % (w.name, args.warmup + args.steps), flush=True)
         return
-    w = ai.WORKLOADS[args.only]
+    w = ai.ALL_WORKLOADS[args.only]
     bits = ai.make_inputs(w.B, w.H, w.S, w.D, w.seed, stress=w.stress, with_dout=w.backward)
     q, k, v = (ai.to_torch_bf16(bits[n], dev) for n in ("q", "k", "v"))
     o = torch.empty_like(q)

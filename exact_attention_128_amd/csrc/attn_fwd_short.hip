@@ -11,8 +11,13 @@
 //     barrier -- a single HBM round trip before any arithmetic;
 //   * one-pass softmax with the exact row maximum (no online rescaling, no
 //     second pass): m = max_j s_ij, P = exp2(s c - m c), then the PV product;
-//   * 4 waves x 32 query rows per workgroup (no ping-pong): all 128 query
-//     rows of one (batch, head).
+//   * 4 waves x 32 query rows per workgroup (no ping-pong), packed by
+//     sequence length so that no wave idles: one head of up to 128 rows, two
+//     heads of up to 64 rows, or four heads of up to 32 rows per workgroup
+//     (the memory-bound side of the roofline, [Tencent, section 2]: many
+//     small heads, each a few KiB of HBM traffic).  A head of at most 64 keys
+//     keeps one 64-key K/V sub-tile in LDS instead of two, which halves the
+//     LDS a head holds and so doubles the heads in flight per CU.
 // The products, fragment layouts and row sums are those of the long-sequence
 // kernel: S^T = K Q^T (32x32x16 bf16 MFMA, A = K from LDS, B = Q in
 // registers, one query row per lane), O^T += V^T P^T with V^T read by the
@@ -23,64 +28,73 @@
 
 namespace attn {
 
-// NSUB 64-key sub-tiles of K and V per head (2 for S <= 128)
-template <int D, bool CAUSAL, int NSUB>
+// WPH waves (32 query rows each) per head, 4 / WPH heads per workgroup; a head
+// has at most 32 * WPH keys, held as NSUB 64-key sub-tiles of K and V in LDS.
+template <int D, bool CAUSAL, int WPH>
 __global__ __launch_bounds__(256) void attn_fwd_short_kernel(FwdParams p) {
   constexpr int NW = 4;
-  constexpr int BR = 32 * NW;
+  constexpr int HPW = NW / WPH;        // heads per workgroup
+  constexpr int NSUB = WPH == 4 ? 2 : 1;
   constexpr int BC = 64;
   constexpr int KK = D / 16;
   constexpr int DB = D / 32;
   constexpr int CH = D / 8;
   constexpr int KSUB = CH * BC * 16;   // K sub-tile [CH][64 keys][16 B]
   constexpr int VSUB = DB * BC * 64;   // V sub-tile [DB][64 keys][64 B]
-  constexpr int NKB = 2 * NSUB;        // 32-key blocks
+  constexpr int HLDS = NSUB * (KSUB + VSUB);   // one head's K and V
+  constexpr int NKB = WPH;             // 32-key blocks that can hold a key
   constexpr int KPIECE = NSUB * CH;    // 1 KiB K pieces: (sub-tile, chunk column)
   constexpr int VPIECE = NSUB * DB * 4;   // (sub-tile, feature block, 16-key group)
-  static_assert(KPIECE % NW == 0 && VPIECE % NW == 0, "pieces must split over the waves");
+  static_assert(NW % WPH == 0 && NKB <= 2 * NSUB, "a head's waves and keys must fit");
+  static_assert(KPIECE % WPH == 0 && VPIECE % WPH == 0, "pieces must split over a head's waves");
 
-  __shared__ __attribute__((aligned(16))) char smem[NSUB * (KSUB + VSUB)];
+  __shared__ __attribute__((aligned(16))) char smem[HPW * HLDS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hs = w / WPH;              // head slot of this wave
+  const int wi = w % WPH;              // wave within the head
   const int l32 = lane & 31;
   const int h = lane >> 5;
   const int S = p.S;
 
-  // work unit (head, 128-row query block); causal: the later (heavier) block first
-  const int u = blockIdx.x;
-  const int bh = u / p.nqb;
-  const int qb = CAUSAL ? p.nqb - 1 - u % p.nqb : u % p.nqb;
-  const int qw = qb * BR + 32 * w;
+  // the head of this wave; a slot past the last head loads nothing and ends
+  // after the barrier
+  const long bhl = (long)blockIdx.x * HPW + hs;
+  const bool live = bhl < p.bh;
+  const int bh = live ? (int)bhl : p.bh - 1;
+  const int qw = 32 * wi;
   const int qrow = qw + l32;
   const size_t head = (size_t)bh * S * D;
 
-  // ---- the burst: K and V of the whole head into LDS (rows past S read as
-  //      zero), split over the four waves, then this lane's Q row
+  // ---- the burst: K and V of the head into LDS (rows past S read as zero),
+  //      split over the head's waves, then this lane's Q row
   const uint32_t hbytes = (uint32_t)S * D * 2;
   const uint16_t* const Kh = p.k + head;
   const uint16_t* const Vh = p.v + head;
-  ATTN_LDS char* const ks = (ATTN_LDS char*)smem;
+  ATTN_LDS char* const ks = (ATTN_LDS char*)smem + hs * HLDS;
   ATTN_LDS char* const vs = ks + NSUB * KSUB;
+  if (live) {
 #pragma unroll
-  for (int k = 0; k < KPIECE / NW; ++k) {
-    const int i = w + NW * k;
-    const int st = i / CH, cc = i % CH;
-    const u32x4 rs = buffer_rsrc_at(Kh, hbytes, (uint32_t)(st * BC) * (2 * D));
-    lds_dma16(ks + st * KSUB + cc * 1024, rs, lane * (2 * D), cc * 16);
-  }
-  const int vl_off = (lane >> 2) * (2 * D) + (lane & 3) * 16;
+    for (int k = 0; k < KPIECE / WPH; ++k) {
+      const int i = wi + WPH * k;
+      const int st = i / CH, cc = i % CH;
+      const u32x4 rs = buffer_rsrc_at(Kh, hbytes, (uint32_t)(st * BC) * (2 * D));
+      lds_dma16(ks + st * KSUB + cc * 1024, rs, lane * (2 * D), cc * 16);
+    }
+    const int vl_off = (lane >> 2) * (2 * D) + (lane & 3) * 16;
 #pragma unroll
-  for (int k = 0; k < VPIECE / NW; ++k) {
-    const int i = w + NW * k;
-    const int st = i / (DB * 4), r = i % (DB * 4), db = r >> 2, rg = r & 3;
-    const u32x4 rs = buffer_rsrc_at(Vh, hbytes, (uint32_t)(st * BC + 16 * rg) * (2 * D));
-    lds_dma16(vs + st * VSUB + db * (BC * 64) + rg * 1024, rs, vl_off, db * 64);
+    for (int k = 0; k < VPIECE / WPH; ++k) {
+      const int i = wi + WPH * k;
+      const int st = i / (DB * 4), r = i % (DB * 4), db = r >> 2, rg = r & 3;
+      const u32x4 rs = buffer_rsrc_at(Vh, hbytes, (uint32_t)(st * BC + 16 * rg) * (2 * D));
+      lds_dma16(vs + st * VSUB + db * (BC * 64) + rg * 1024, rs, vl_off, db * 64);
+    }
   }
   bf16x8 qf[KK];
   {
-    const bool ok = qrow < S;
+    const bool ok = live && qrow < S;
     const uint16_t* qr = p.q + head + (size_t)(ok ? qrow : S - 1) * D + 8 * h;
     const uint32_t qm = ok ? p.qand : 0u;
 #pragma unroll
@@ -95,7 +109,8 @@ __global__ __launch_bounds__(256) void attn_fwd_short_kernel(FwdParams p) {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
-  if (qw >= S) return;   // a wave with no valid row (after the barrier: its loads are in)
+  // a wave with no head or no valid row (after the barrier: its loads are in)
+  if (!live || qw >= S) return;
 
   // ---- S^T = K Q^T over every key; s[b] = 32-key block b (key 32b + 8(r/4) +
   //      4h + r%4 of register r, query qrow)
@@ -152,7 +167,7 @@ __global__ __launch_bounds__(256) void attn_fwd_short_kernel(FwdParams p) {
   const int vbase = (4 * ((lane >> 4) >> 1) + ((lane & 15) >> 2)) * 64 +
                     (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
 #pragma unroll
-  for (int g = 0; g < 4 * NSUB; ++g) {
+  for (int g = 0; g < 2 * NKB; ++g) {
     const uint32_t* pp = &pk[g >> 1][4 * (g & 1)];
     const u32x4 pw = {pp[0], pp[1], pp[2], pp[3]};
 #pragma unroll
@@ -184,22 +199,29 @@ __global__ __launch_bounds__(256) void attn_fwd_short_kernel(FwdParams p) {
   }
 }
 
-template <int D, bool CAUSAL, int NSUB>
-static hipError_t launch_short_t(const FwdParams& p0, hipStream_t stream) {
-  FwdParams p = p0;
-  p.nqb = (p.S + 127) / 128;
-  const long grid = (long)p.bh * p.nqb;
-  if (grid <= 0 || grid * 256 > 0xffffffffL) return hipErrorInvalidConfiguration;
-  void* args[] = {&p};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_short_kernel<D, CAUSAL, NSUB>),
+template <int D, bool CAUSAL, int WPH>
+static hipError_t launch_short_t(const FwdParams& p, hipStream_t stream) {
+  constexpr int HPW = 4 / WPH;
+  const long grid = ((long)p.bh + HPW - 1) / HPW;
+  if (p.bh <= 0 || grid * 256 > 0xffffffffL) return hipErrorInvalidConfiguration;
+  FwdParams pp = p;
+  void* args[] = {&pp};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_short_kernel<D, CAUSAL, WPH>),
                          dim3((unsigned)grid), dim3(256), args, 0, stream);
 }
 
+template <int D, bool CAUSAL>
+static hipError_t launch_short_d(const FwdParams& p, hipStream_t stream) {
+  if (p.S <= 32) return launch_short_t<D, CAUSAL, 1>(p, stream);
+  if (p.S <= 64) return launch_short_t<D, CAUSAL, 2>(p, stream);
+  return launch_short_t<D, CAUSAL, 4>(p, stream);
+}
+
 hipError_t launch_fwd_short(const FwdParams& p, int D, bool causal, hipStream_t stream) {
-  static_assert(kShortMaxS <= 2 * 64, "two 64-key sub-tiles hold every key");
+  static_assert(kShortMaxS <= 4 * 32, "four waves of 32 rows hold every query row of a head");
   if (p.S < 1 || p.S > kShortMaxS) return hipErrorInvalidValue;
-  if (D == 128) return causal ? launch_short_t<128, true, 2>(p, stream) : launch_short_t<128, false, 2>(p, stream);
-  if (D == 64) return causal ? launch_short_t<64, true, 2>(p, stream) : launch_short_t<64, false, 2>(p, stream);
+  if (D == 128) return causal ? launch_short_d<128, true>(p, stream) : launch_short_d<128, false>(p, stream);
+  if (D == 64) return causal ? launch_short_d<64, true>(p, stream) : launch_short_d<64, false>(p, stream);
   return hipErrorInvalidValue;
 }
 

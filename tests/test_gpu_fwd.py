@@ -44,6 +44,25 @@ def test_short_sequence_many_blocks(causal):
     P.assert_fwd_ok(err, "short many blocks causal=%s" % causal)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("S,heads", [(1, 5), (9, 7), (32, 6), (33, 3), (50, 9), (64, 5), (65, 3)])
+def test_short_sequence_packed_heads(S, heads, D, causal):
+    """Heads packed per workgroup: four heads of <= 32 rows, or two of <= 64
+    rows, per workgroup.  Head counts that leave one to three slots of the
+    last workgroup empty, every element against the oracle."""
+    err = _full_case(1, heads, S, D, causal, seed=2100 + S + heads + D + int(causal))
+    P.assert_fwd_ok(err, "packed S=%d heads=%d D=%d causal=%s" % (S, heads, D, causal))
+
+
+@pytest.mark.parametrize("S", [24, 64])
+def test_short_sequence_packed_many_heads(S):
+    """Many packed workgroups: 2001 heads (not a multiple of 2 or 4), every
+    element against the oracle."""
+    err = _full_case(3, 667, S, 128, True, seed=2200 + S)
+    P.assert_fwd_ok(err, "packed many heads S=%d" % S)
+
+
 def test_short_sequence_counting_makes_no_tests():
     """At S <= 128 the counting entry runs the one-pass kernel, which makes no
     rescale test: zero events, and the same bits as attn_fwd_ex."""
@@ -212,12 +231,13 @@ def test_non_default_stream():
     P.assert_fwd_ok(P.fwd_errors(o, lse, o_ref, lse_ref), "side stream")
 
 
-@pytest.mark.parametrize("name", ["fwd_s2k", "fwd_causal_s8k", "fwd_stress_s16k"])
+@pytest.mark.parametrize("name", ["fwd_s2k", "fwd_causal_s8k", "fwd_stress_s16k",
+                                  *ai.SHORT_WORKLOADS])
 def test_full_size_workloads(name):
     """Full-size workloads in the benchmark's launch configuration, every element
     of O and LSE against the oracle (about 10 s of oracle time each for the two
-    long causal ones)."""
-    w = ai.WORKLOADS[name]
+    long causal ones), including the many-head short-sequence workloads."""
+    w = ai.ALL_WORKLOADS[name]
     bits = ai.workload_inputs(w)
     o, lse, _ = P.gpu_fwd(bits, w.causal, w.scale)
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
