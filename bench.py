@@ -13,8 +13,14 @@ Also measured, in the same process:
     HIP events on the stream it is launched on -> "roofline" (MFMA bound); the
     backward's dQ kernel likewise -> "dq_kernel";
   * the forward alone on the four forward workloads (S=128 D=64 non-causal, a
-    latency/HBM case reported with its algorithmic HBM rate; S=2048 non-causal;
+    latency case reported with its algorithmic HBM rate; S=2048 non-causal;
     S=8192 causal; S=16384 causal rising-maximum) -> "legs" and "fwd_roofline";
+  * the forward on three many-head short-sequence workloads (S=128, 64, 32),
+    bound by HBM, each with its algorithmic HBM rate -> "legs" and
+    "short_roofline" (HBM bound, S=128);
+  * the FP8 (E4M3) forward on the S=8192 causal shape against the FP8 peak;
+  * calibration legs that are not on the path: a library bf16 GEMM (what the
+    matrix cores sustain) and a 1 GiB device copy (what HBM sustains);
   * the fp64 CPU oracle on a bounded sample of the same workload on this host's
     cores -> "cpu_baseline" (a reported baseline, not the target).
 
@@ -511,6 +517,7 @@ def main():
     legs = {}
     cpu_legs = {}
     fwd_roof = None
+    short_roof = None
     gemm_tflops = None
     if not args.no_cpu_baseline:
         import oracle
@@ -607,6 +614,31 @@ def main():
             ms, tf, 100 * tf / PEAK_BF16_TFLOPS))
         del ga, gb, gc
         torch.cuda.empty_cache()
+        # Context for the HBM peak: a plain 1 GiB device-to-device copy (torch's
+        # copy kernel; 2 GiB moved per launch) timed the same way.  Not part of
+        # the attention path.
+        nb = 1 << 30
+        csrc = torch.ones(nb, dtype=torch.uint8, device=dev)
+        cdst = torch.empty_like(csrc)
+        for _ in range(3):
+            cdst.copy_(csrc)
+        ms = time_launches(lambda: cdst.copy_(csrc), n_rep)
+        copy_gbs = 2.0 * nb / (ms * 1e-3) / 1e9
+        legs["device_copy"] = {"op": "torch copy_ of 1 GiB (read + write)", "ms": round(ms, 4),
+                               "median_ms": round(last_median(), 4), "hbm_gbs": round(copy_gbs, 1),
+                               "hbm_frac": round(copy_gbs / PEAK_HBM_GBS, 4)}
+        log("device copy (1 GiB): %.4f ms  %.1f GB/s (%.1f%% of %.0f)" % (
+            ms, copy_gbs, 100 * copy_gbs / PEAK_HBM_GBS, PEAK_HBM_GBS))
+        del csrc, cdst
+        torch.cuda.empty_cache()
+        for name in ai.SHORT_WORKLOADS:
+            legs[name]["hbm_frac_vs_device_copy"] = round(legs[name]["hbm_gbs"] / copy_gbs, 4)
+        sh = legs["fwd_short_s128_h4096"]
+        short_roof = {"kernel": "attn_fwd_short_kernel<128,non-causal>",
+                      "workload": "fwd_short_s128_h4096", "bound": "hbm",
+                      "achieved": sh["hbm_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                      "frac": sh["hbm_frac"], "ms": sh["ms"], "median_ms": sh["median_ms"],
+                      "frac_vs_device_copy": sh["hbm_frac_vs_device_copy"]}
         c3 = legs["fwd_causal_s8k"]
         fwd_roof = {"kernel": "attn_fwd_kernel<128,causal>", "workload": "fwd_causal_s8k",
                     "bound": "mfma", "achieved": c3["tflops"], "peak": PEAK_BF16_TFLOPS,
@@ -670,6 +702,7 @@ def main():
         "fwd_tflops": round(f_fwd / (ms_fwd * 1e-3) / 1e12, 1),
         "bwd_tflops": round(f_bwd / (ms_bwd * 1e-3) / 1e12, 1),
         "fwd_roofline": fwd_roof,
+        "short_roofline": short_roof,
         "legs": legs,
         "cpu_baseline": cpu,
     }

@@ -15,9 +15,10 @@
 //     sequence length so that no wave idles: one head of up to 128 rows, two
 //     heads of up to 64 rows, or four heads of up to 32 rows per workgroup
 //     (the memory-bound side of the roofline, [Tencent, section 2]: many
-//     small heads, each a few KiB of HBM traffic).  A head of at most 64 keys
-//     keeps one 64-key K/V sub-tile in LDS instead of two, which halves the
-//     LDS a head holds and so doubles the heads in flight per CU.
+//     small heads, each a few KiB of HBM traffic).  A head keeps only the K/V
+//     rows it can have in LDS -- two 64-key sub-tiles for up to 128 keys, one
+//     for up to 64, one of 32 keys for up to 32 -- so the LDS a head holds,
+//     which bounds the heads in flight per CU, shrinks with the sequence.
 // The products, fragment layouts and row sums are those of the long-sequence
 // kernel: S^T = K Q^T (32x32x16 bf16 MFMA, A = K from LDS, B = Q in
 // registers, one query row per lane), O^T += V^T P^T with V^T read by the
@@ -29,22 +30,28 @@
 namespace attn {
 
 // WPH waves (32 query rows each) per head, 4 / WPH heads per workgroup; a head
-// has at most 32 * WPH keys, held as NSUB 64-key sub-tiles of K and V in LDS.
+// has at most 32 * WPH keys, held as NSUB sub-tiles of BC keys of K and V in
+// LDS (BC = 32 when WPH = 1, else 64).
 template <int D, bool CAUSAL, int WPH>
 __global__ __launch_bounds__(256) void attn_fwd_short_kernel(FwdParams p) {
   constexpr int NW = 4;
   constexpr int HPW = NW / WPH;        // heads per workgroup
   constexpr int NSUB = WPH == 4 ? 2 : 1;
-  constexpr int BC = 64;
+  constexpr int BC = WPH == 1 ? 32 : 64;
+  constexpr int NG = BC / 16;          // 16-key groups per sub-tile
+  constexpr int KB = BC / 32;          // 32-key blocks per sub-tile
   constexpr int KK = D / 16;
   constexpr int DB = D / 32;
   constexpr int CH = D / 8;
-  constexpr int KSUB = CH * BC * 16;   // K sub-tile [CH][64 keys][16 B]
-  constexpr int VSUB = DB * BC * 64;   // V sub-tile [DB][64 keys][64 B]
+  constexpr int KSUB = CH * BC * 16;   // K sub-tile [CH][BC keys][16 B]
+  constexpr int VSUB = DB * BC * 64;   // V sub-tile [DB][BC keys][64 B]
   constexpr int HLDS = NSUB * (KSUB + VSUB);   // one head's K and V
   constexpr int NKB = WPH;             // 32-key blocks that can hold a key
-  constexpr int KPIECE = NSUB * CH;    // 1 KiB K pieces: (sub-tile, chunk column)
-  constexpr int VPIECE = NSUB * DB * 4;   // (sub-tile, feature block, 16-key group)
+  // 1 KiB pieces of one DMA instruction each: K (sub-tile, chunk column) for
+  // 64-key sub-tiles, two adjacent chunk columns for 32-key ones; V
+  // (sub-tile, feature block, 16-key group)
+  constexpr int KPIECE = NSUB * CH * BC / 64;
+  constexpr int VPIECE = NSUB * DB * NG;
   static_assert(NW % WPH == 0 && NKB <= 2 * NSUB, "a head's waves and keys must fit");
   static_assert(KPIECE % WPH == 0 && VPIECE % WPH == 0, "pieces must split over a head's waves");
 
@@ -79,15 +86,21 @@ __global__ __launch_bounds__(256) void attn_fwd_short_kernel(FwdParams p) {
 #pragma unroll
     for (int k = 0; k < KPIECE / WPH; ++k) {
       const int i = wi + WPH * k;
-      const int st = i / CH, cc = i % CH;
-      const u32x4 rs = buffer_rsrc_at(Kh, hbytes, (uint32_t)(st * BC) * (2 * D));
-      lds_dma16(ks + st * KSUB + cc * 1024, rs, lane * (2 * D), cc * 16);
+      if constexpr (BC == 64) {
+        const int st = i / CH, cc = i % CH;
+        const u32x4 rs = buffer_rsrc_at(Kh, hbytes, (uint32_t)(st * BC) * (2 * D));
+        lds_dma16(ks + st * KSUB + cc * 1024, rs, lane * (2 * D), cc * 16);
+      } else {
+        // lanes 0-31: key l32 of chunk column 2i, lanes 32-63: of column 2i+1
+        const u32x4 rs = buffer_rsrc_at(Kh, hbytes, 0u);
+        lds_dma16(ks + i * 1024, rs, l32 * (2 * D) + h * 16, i * 32);
+      }
     }
     const int vl_off = (lane >> 2) * (2 * D) + (lane & 3) * 16;
 #pragma unroll
     for (int k = 0; k < VPIECE / WPH; ++k) {
       const int i = wi + WPH * k;
-      const int st = i / (DB * 4), r = i % (DB * 4), db = r >> 2, rg = r & 3;
+      const int st = i / (DB * NG), r = i % (DB * NG), db = r / NG, rg = r % NG;
       const u32x4 rs = buffer_rsrc_at(Vh, hbytes, (uint32_t)(st * BC + 16 * rg) * (2 * D));
       lds_dma16(vs + st * VSUB + db * (BC * 64) + rg * 1024, rs, vl_off, db * 64);
     }
@@ -122,7 +135,7 @@ __global__ __launch_bounds__(256) void attn_fwd_short_kernel(FwdParams p) {
     for (int r = 0; r < 16; ++r) s[b][r] = 0.0f;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      const bf16x8 a = lds_read_b128(ks + (b >> 1) * KSUB + 2 * kk * (BC * 16) + 32 * (b & 1) * 16 +
+      const bf16x8 a = lds_read_b128(ks + (b / KB) * KSUB + 2 * kk * (BC * 16) + 32 * (b % KB) * 16 +
                                      kbase);
       s[b] = mfma32(a, qf[kk], s[b]);
     }
@@ -158,7 +171,7 @@ __global__ __launch_bounds__(256) void attn_fwd_short_kernel(FwdParams p) {
     }
   }
 
-  // ---- O^T += V^T P^T over every 16-key group g (sub-tile g/4, group g%4)
+  // ---- O^T += V^T P^T over every 16-key group g (sub-tile g/NG, group g%NG)
   f32x16 o[DB];
 #pragma unroll
   for (int i = 0; i < DB; ++i)
@@ -172,7 +185,7 @@ __global__ __launch_bounds__(256) void attn_fwd_short_kernel(FwdParams p) {
     const u32x4 pw = {pp[0], pp[1], pp[2], pp[3]};
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      const ATTN_LDS char* rb = vs + vbase + (g >> 2) * VSUB + 16 * (g & 3) * 64 + db * (BC * 64);
+      const ATTN_LDS char* rb = vs + vbase + (g / NG) * VSUB + 16 * (g % NG) * 64 + db * (BC * 64);
       const u32x2 a0 = __builtin_bit_cast(u32x2, lds_read_tr16(rb));
       const u32x2 a1 = __builtin_bit_cast(u32x2, lds_read_tr16(rb + 8 * 64));
       const u32x4 aw = {a0[0], a0[1], a1[0], a1[1]};
