@@ -106,19 +106,20 @@ def oracle_fwd_sample(w, bits, budget_s):
         return {"tflops": round(full / dt / 1e12, 6), "seconds": round(dt, 3),
                 "sample": "whole workload"}
     q, k, v = (bits[n].reshape(B * H, S, D) for n in ("q", "k", "v"))
+    n = min(64, S)   # rows per chunk: evenly spaced, distinct
     flops, rows, chunk, t0 = 0.0, 0, 0, time.perf_counter()
     while time.perf_counter() - t0 < budget_s and rows < B * H * S:
         hd = chunk % (B * H)
-        pos = (np.arange(64, dtype=np.int64) * (S // 64) + (chunk * 7919) % max(1, S // 64)) % S
+        pos = (np.arange(n, dtype=np.int64) * (S // n) + (chunk * 7919) % (S // n)) % S
         oracle.attn_fwd_rows(ai.bf16_bits_to_f64(q[hd, pos]), pos, ai.bf16_bits_to_f64(k[hd]),
                              ai.bf16_bits_to_f64(v[hd]), w.scale, w.causal)
         flops += oracle.rows_flops(pos, S, D, w.causal)
-        rows += 64
+        rows += n
         chunk += 1
     dt = time.perf_counter() - t0
     return {"tflops": round(flops / dt / 1e12, 6), "seconds": round(dt, 3),
-            "sample": "%d query rows (64-row chunks spread over the sequence, %d heads) of %d" % (
-                rows, min(chunk, B * H), B * H * S)}
+            "sample": "%d query rows (%d-row chunks spread over the sequence, %d heads) of %d" % (
+                rows, n, min(chunk, B * H), B * H * S)}
 
 
 def _grids(w):
