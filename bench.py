@@ -45,13 +45,17 @@ PEAK_HBM_GBS = 8000.0
 # HBM bytes per launch of the dominant kernel (the backward's dK/dV kernel on
 # the causal S=4096 workload), from rocprofv3 FETCH_SIZE and WRITE_SIZE runs
 # (profiles/bwd_causal_s4k_counters.md), each scaled by what the same counter
-# reads for a plain 1 GiB device copy.  Valid only for the kernel sources whose
-# digest is recorded here; reported as null once they change.
+# reads for a plain 1 GiB device copy; and the shader clock the kernel ran at
+# in those counter runs (GRBM_GUI_ACTIVE per XCD over the dispatch duration),
+# which prices the dense peak at the clock the power limit leaves.  Valid only
+# for the kernel sources whose digest is recorded here; reported as null once
+# they change.
 TRAFFIC_SOURCES = ("exact_attention_128_amd/csrc/attn_bwd.hip",
                    "exact_attention_128_amd/csrc/gfx950.h",
                    "exact_attention_128_amd/csrc/attn_internal.h",
                    "exact_attention_128_amd/build.py")
 TRAFFIC = {"workload": "bwd_causal_s4k", "read_bytes": 224928572, "write_bytes": 67108864,
+           "clock_ghz": 1.976,
            "sources_sha256": "07c2b146a8577265a693c26a1825807faa0a3731f28ee9ad053f07e5d847337b"}
 # the same for the forward on the causal S=8192 workload
 # (profiles/fwd_causal_s8k_counters.md)
@@ -60,10 +64,13 @@ FWD_TRAFFIC_SOURCES = ("exact_attention_128_amd/csrc/attn_fwd.hip",
                        "exact_attention_128_amd/csrc/attn_internal.h",
                        "exact_attention_128_amd/build.py")
 FWD_TRAFFIC = {"workload": "fwd_causal_s8k", "read_bytes": 1388079682, "write_bytes": 136322645,
+               "clock_ghz": 1.661,
                "sources_sha256": "487266126d82623c9e07cf5c24d0a9cbe48ef959f837bc3892eba838e2125165"}
 
 
-def measured_traffic(workload, record=None, sources=None):
+def measured_record(workload, record=None, sources=None):
+    """The profiled record of a kernel on a workload, or None when it was taken
+    on another workload or the kernel's sources have changed since."""
     import hashlib
     record = TRAFFIC if record is None else record
     sources = TRAFFIC_SOURCES if sources is None else sources
@@ -75,7 +82,22 @@ def measured_traffic(workload, record=None, sources=None):
             h.update(fh.read())
     if h.hexdigest() != record["sources_sha256"]:
         return None
-    return record["read_bytes"] + record["write_bytes"]
+    return record
+
+
+def measured_traffic(workload, record=None, sources=None):
+    rec = measured_record(workload, record, sources)
+    return None if rec is None else rec["read_bytes"] + rec["write_bytes"]
+
+
+def at_profiled_clock(achieved, peak, workload, record=None, sources=None):
+    """(clock GHz, achieved / the dense peak at that clock) from the profiled
+    record, or (None, None)."""
+    rec = measured_record(workload, record, sources)
+    if rec is None or "clock_ghz" not in rec:
+        return None, None
+    g = rec["clock_ghz"]
+    return g, round(achieved / (peak * g / 2.4), 4)
 
 
 def log(*a):
@@ -219,14 +241,21 @@ def pmc_command(n, workload, outdir="gpurun_out/pmc"):
 
 
 def _pmc_load(path):
-    """{kernel name: {counter: mean per-dispatch value}} of one counter CSV."""
+    """{kernel name: {counter: mean per-dispatch value}} of one counter CSV,
+    plus "_duration_ns": the mean dispatch duration from its timestamps."""
     import csv
-    per = {}
+    per, dur = {}, {}
     with open(path) as fh:
         for r in csv.DictReader(fh):
-            per.setdefault(r["Kernel_Name"], {}).setdefault(r["Counter_Name"], []).append(
-                float(r["Counter_Value"]))
-    return {k: {c: sum(v) / len(v) for c, v in d.items()} for k, d in per.items()}
+            k = r["Kernel_Name"]
+            per.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+            if "Start_Timestamp" in r and r["Start_Timestamp"]:
+                dur.setdefault(k, {})[r["Dispatch_Id"]] = (int(r["End_Timestamp"]) -
+                                                            int(r["Start_Timestamp"]))
+    out = {k: {c: sum(v) / len(v) for c, v in d.items()} for k, d in per.items()}
+    for k, d in dur.items():
+        out[k]["_duration_ns"] = sum(d.values()) / len(d)
+    return out
 
 
 def _alg_bytes(fam, w):
@@ -258,9 +287,15 @@ def pmc_summary(root, workload):
     cf = copy_kernel(_pmc_load(csvf(3, "copy")))["FETCH_SIZE"]
     cw = copy_kernel(_pmc_load(csvf(4, "copy")))["WRITE_SIZE"]
     fs, ws = 1048576.0 / cf, 1048576.0 / cw
-    raw = {}
+    raw, clk = {}, {}
     for n in PMC_PASSES:
         for k, d in _pmc_load(csvf(n, workload)).items():
+            if "GRBM_GUI_ACTIVE" in d and "_duration_ns" in d:
+                # the clock the kernel ran at in this pass: busy cycles per XCD
+                # over the dispatch's duration
+                clk.setdefault(k, []).append((d["GRBM_GUI_ACTIVE"] / 8 / d["_duration_ns"],
+                                              d["_duration_ns"]))
+            d.pop("_duration_ns", None)
             raw.setdefault(k, {}).update(d)
     short = lambda k: k.replace("void ", "").split("(")[0]
     fam = lambda k: short(k).split("<")[0].split("::")[-1]
@@ -308,6 +343,36 @@ def pmc_summary(root, workload):
                      d["SQ_INSTS_LDS"], d["SQ_LDS_BANK_CONFLICT"],
                      d["FETCH_SIZE"] * 1024 * fs / 1e6, mb(ar), d["WRITE_SIZE"] * 1024 * ws / 1e6,
                      mb(aw)))
+    if clk:
+        o.append("\nMeasured clock.  Shader clock while profiled = `GRBM_GUI_ACTIVE` / 8 XCDs / the "
+                 "dispatch's duration (its start and end timestamps), averaged over the passes that "
+                 "hold the counter.  Dense peak at that clock = 2516.6 TFLOPS x clock / 2.4 GHz "
+                 "(FP8: twice).  Achieved = the kernel's credited algorithmic flops over the same "
+                 "mean duration:\n")
+        o.append("| Kernel | clock (GHz) | mean duration (us) | dense peak at that clock (TFLOPS) "
+                 "| achieved (TFLOPS) | fraction of the peak at that clock | fraction of the "
+                 "2.4 GHz peak |")
+        o.append("|---|---|---|---|---|---|---|")
+        for k in order:
+            if k in clk:
+                g = sum(c for c, _ in clk[k]) / len(clk[k])
+                du = sum(t for _, t in clk[k]) / len(clk[k])
+                pk = (PEAK_FP8_TFLOPS if fam(k) == "attn_fwd_fp8_kernel" else PEAK_BF16_TFLOPS)
+                fl = None
+                if fam(k) in _CREDIT:
+                    kind, share = _CREDIT[fam(k)]
+                    fl = share * fwd_flops(w.B, w.H, w.S, w.D, w.causal) * (2.5 if kind == "bwd" else 1.0)
+                    if kind == "bwd" and not w.backward:
+                        fl = None
+                    if kind == "fwd" and w.backward and fam(k) == "attn_fwd_kernel":
+                        fl = fwd_flops(w.B, w.H, w.S, w.D, w.causal)
+                if fl is None:
+                    o.append("| `%s` | %.3f | %.1f | %.1f | - | - | - |" % (short(k), g, du / 1e3,
+                                                                             pk * g / 2.4))
+                else:
+                    t = fl / (du * 1e-9) / 1e12
+                    o.append("| `%s` | %.3f | %.1f | %.1f | %.1f | %.4f | %.4f |" % (
+                        short(k), g, du / 1e3, pk * g / 2.4, t, t / (pk * g / 2.4), t / pk))
     o.append("\nHBM bytes per launch (scaled): " + "; ".join(
         "`%s` read %d, write %d" % (fam(k), round(raw[k]["FETCH_SIZE"] * 1024 * fs),
                                     round(raw[k]["WRITE_SIZE"] * 1024 * ws)) for k in order) + "\n")
@@ -647,6 +712,8 @@ def main():
                     "median_ms": c3["median_ms"], "frac_median": c3["frac_peak_median"],
                     "frac_vs_library_gemm": round(c3["tflops"] / gemm_tflops, 4),
                     "traffic": measured_traffic("fwd_causal_s8k", FWD_TRAFFIC, FWD_TRAFFIC_SOURCES)}
+        fwd_roof["clock_ghz_profiled"], fwd_roof["frac_at_profiled_clock"] = at_profiled_clock(
+            c3["tflops"], PEAK_BF16_TFLOPS, "fwd_causal_s8k", FWD_TRAFFIC, FWD_TRAFFIC_SOURCES)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -666,6 +733,7 @@ def main():
                "per_config": cpu_legs}
         log("cpu oracle: %s" % cpu)
 
+    main_clk = at_profiled_clock(main_tflops, PEAK_BF16_TFLOPS, w.name)
     out = {
         "metric": "attention fwd/bwd TFLOPS (bf16, D=128) and % of MI355X bf16 MFMA peak",
         "value": round(value, 2),
@@ -689,7 +757,8 @@ def main():
                      "frac_median": round(0.8 * f_bwd / (med_main * 1e-3) / 1e12 /
                                           PEAK_BF16_TFLOPS, 4),
                      "frac_vs_library_gemm": (round(main_tflops / gemm_tflops, 4)
-                                              if gemm_tflops else None)},
+                                              if gemm_tflops else None),
+                     "clock_ghz_profiled": main_clk[0], "frac_at_profiled_clock": main_clk[1]},
         "dq_kernel": {"kernel": "attn_bwd_dq_kernel<128,causal>", "ms": round(ms_dq, 4),
                       "median_ms": round(med_dq, 4),
                       "algorithmic_tflops": round(dq_alg_tflops, 1),

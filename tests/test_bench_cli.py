@@ -133,3 +133,19 @@ def test_pmc_summary_scales_bytes_by_the_copy(tmp_path):
     assert cells[11] == "%.1f" % (1000 * 1024 * 2 / 1e6)
     assert cells[13] == "%.1f" % (3000 * 1024 / 1e6)
     assert "read %d, write %d" % (1000 * 1024 * 2, 3000 * 1024) in md
+
+
+def test_clock_record_prices_the_peak_at_that_clock(tmp_path):
+    """at_profiled_clock divides the achieved rate by the dense peak scaled to
+    the recorded clock, and gives nothing once the sources change."""
+    import hashlib
+    b = _bench()
+    src = tmp_path / "k.hip"
+    src.write_bytes(b"v1")
+    rel = os.path.relpath(str(src), ROOT)
+    rec = {"workload": "w", "read_bytes": 1, "write_bytes": 1, "clock_ghz": 1.2,
+           "sources_sha256": hashlib.sha256(b"v1").hexdigest()}
+    g, frac = b.at_profiled_clock(629.15, 2516.6, "w", rec, (rel,))
+    assert g == 1.2 and frac == 0.5
+    src.write_bytes(b"v2")
+    assert b.at_profiled_clock(629.15, 2516.6, "w", rec, (rel,)) == (None, None)
