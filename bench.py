@@ -54,18 +54,18 @@ TRAFFIC_SOURCES = ("exact_attention_128_amd/csrc/attn_bwd.hip",
                    "exact_attention_128_amd/csrc/gfx950.h",
                    "exact_attention_128_amd/csrc/attn_internal.h",
                    "exact_attention_128_amd/build.py")
-TRAFFIC = {"workload": "bwd_causal_s4k", "read_bytes": 224928572, "write_bytes": 67108864,
-           "clock_ghz": 1.976,
-           "sources_sha256": "07c2b146a8577265a693c26a1825807faa0a3731f28ee9ad053f07e5d847337b"}
+TRAFFIC = {"workload": "bwd_causal_s4k", "read_bytes": 229366563, "write_bytes": 67108864,
+           "clock_ghz": 1.924,
+           "sources_sha256": "53d46275cb26cea5975d3e66432fbe296b0dfe8fbf3f39b86cf9decf60de397c"}
 # the same for the forward on the causal S=8192 workload
 # (profiles/fwd_causal_s8k_counters.md)
 FWD_TRAFFIC_SOURCES = ("exact_attention_128_amd/csrc/attn_fwd.hip",
                        "exact_attention_128_amd/csrc/gfx950.h",
                        "exact_attention_128_amd/csrc/attn_internal.h",
                        "exact_attention_128_amd/build.py")
-FWD_TRAFFIC = {"workload": "fwd_causal_s8k", "read_bytes": 1388079682, "write_bytes": 136322645,
-               "clock_ghz": 1.661,
-               "sources_sha256": "487266126d82623c9e07cf5c24d0a9cbe48ef959f837bc3892eba838e2125165"}
+FWD_TRAFFIC = {"workload": "fwd_causal_s8k", "read_bytes": 1383148222, "write_bytes": 136329493,
+               "clock_ghz": 1.542,
+               "sources_sha256": "f0d65c5b54bd6e2dcf5025f762d4e7f38e5c2372263b38846633ebbf538d3b16"}
 
 
 def measured_record(workload, record=None, sources=None):

@@ -64,13 +64,21 @@ def load():
                 raise ImportError(
                     "libattn.so is not built (expected at %s); run "
                     "`python exact_attention_128_amd/build.py` (hipcc, gfx950)" % _LIB_PATH)
-            lib = ctypes.CDLL(_LIB_PATH)
-            for name, (res, args) in SIGNATURES.items():
-                fn = getattr(lib, name)
-                fn.restype = res
-                fn.argtypes = args
-            _lib = lib
+            _lib = open_library(_LIB_PATH)
     return _lib
+
+
+def open_library(path: str):
+    """A ctypes handle on a library exporting the C ABI at path, with every
+    signature set (also used to open the LDS race-check build,
+    libattn_lds_poison.so, beside the product library)."""
+    import torch  # noqa: F401  -- shares its libamdhip64 with the library
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
 
 
 def raise_for(rc: int, where: str) -> None:

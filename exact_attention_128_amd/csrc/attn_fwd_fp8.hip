@@ -179,7 +179,7 @@ void attn_fwd_fp8_kernel(Fp8FwdParams p) {
       const int i = (w & 3) + 4 * k;
       const int u = i / CH, cc = i % CH;
       const u32x4 rs = buffer_rsrc_at(src, hbytes, (uint32_t)(key0 + u * BC) * D);
-      lds_dma16(base + u * T::SUB + cc * CSTR, rs, lane * D, cc * 16);
+      lds_dma16(base + u * T::SUB + cc * CSTR, rs, lane * D, cc * 16, kPoisonE4M3);
     }
   };
   auto fetch_k = [&](int st) { fetch(Kh, kring + (st % T::NKS) * T::SLOT, st); };

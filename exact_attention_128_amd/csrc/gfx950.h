@@ -73,9 +73,32 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const ATTN_LDS char* p) {
 // waits for it in front of unrelated LDS reads.  The memory clobber keeps LDS
 // accesses from moving across it.
 // (Nothing else in these kernels uses m0, so clobbering it is safe.)
+//
+// LDS race check (debug build, compiled with ATTN_LDS_POISON=1 into
+// libattn_lds_poison.so): before each such load the lane writes a NaN pattern
+// over the 16 bytes the load will land, and waits for that write.  A wave
+// that reads a piece before the load's wait and barrier -- a missing wait, or
+// a refill that overtakes the piece's last reader -- then reads NaN instead of
+// an older tile, and the NaN reaches the outputs; so does a load that leaves
+// its bytes unwritten (rows past the end must land as zeros).
+#ifndef ATTN_LDS_POISON
+#define ATTN_LDS_POISON 0
+#endif
+constexpr uint32_t kPoisonBf16 = 0x7FC07FC0u;   // bf16 NaN pairs, also an fp32 NaN
+constexpr uint32_t kPoisonE4M3 = 0x7F7F7F7Fu;   // E4M3 NaN bytes
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void lds_dma16(ATTN_LDS char* dst, u32x4 rsrc, int voff, int soff) {
+__device__ __forceinline__ void lds_dma16(ATTN_LDS char* dst, u32x4 rsrc, int voff, int soff,
+                                          uint32_t poison = kPoisonBf16) {
+  if constexpr (ATTN_LDS_POISON != 0) {
+    const int lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    ATTN_LDS uint32_t* const d = (ATTN_LDS uint32_t*)(dst + 16 * lane);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) d[e] = poison;   // four 4-byte stores: one register
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the pattern has landed
+  } else {
+    (void)poison;
+  }
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :
                : "s"((uint32_t)(uintptr_t)dst), "v"(voff), "s"(rsrc), "s"(soff)

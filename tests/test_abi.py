@@ -31,6 +31,18 @@ def test_header_symbols_exported(lib):
         assert hasattr(raw, n), "symbol %s declared in attn.h but not exported" % n
 
 
+def test_race_check_build_exports_the_same_abi():
+    """The LDS race-check build (libattn_lds_poison.so) is the same C ABI, and
+    rejects a bad request the same way (host-side checks before any HIP call)."""
+    from exact_attention_128_amd import _lib
+    path = os.path.join(ROOT, "exact_attention_128_amd", "libattn_lds_poison.so")
+    poison = _lib.open_library(path)
+    for n in _declared():
+        assert hasattr(poison, n), "symbol %s missing from the race-check build" % n
+    assert poison.attn_version() == _lib.load().attn_version()
+    assert _fwd(poison, D=96) == 3   # ATTN_ERR_HEAD_DIM, no device touched
+
+
 def test_binding_signatures_cover_header():
     from exact_attention_128_amd import _lib
     assert sorted(_lib.SIGNATURES) == _declared()
