@@ -232,9 +232,9 @@ PMC_PASSES = {
 }
 
 
-def pmc_command(n, workload, outdir="gpurun_out/pmc"):
-    """The rocprofv3 command of counter pass n over one workload (run from the
-    repository root)."""
+def pmc_command(n, workload, outdir):
+    """The rocprofv3 command of counter pass n over one workload, writing under
+    outdir (run from the repository root)."""
     return ("rocprofv3 --pmc %s --output-format csv -d %s/p%d_%s -o run -- "
             "python3 bench.py --only %s --steps 2 --warmup 1" % (PMC_PASSES[n], outdir, n,
                                                                   workload, workload))
@@ -305,9 +305,9 @@ def pmc_summary(root, workload):
         "Collected on one MI355X, each counter set in its own run, from the repository root "
         "(the profiler wants `cd /tmp && export TMPDIR=/tmp` first and then absolute paths "
         "to the same files), then summarised by the last command:\n", "```"]
-    o += [pmc_command(n, workload) for n in PMC_PASSES]
-    o += [pmc_command(n, "copy") for n in (3, 4)]
-    o += ["python3 bench.py --pmc-summary gpurun_out/pmc %s" % workload, "```\n"]
+    o += [pmc_command(n, workload, root) for n in PMC_PASSES]
+    o += [pmc_command(n, "copy", root) for n in (3, 4)]
+    o += ["python3 bench.py --pmc-summary %s %s" % (root, workload), "```\n"]
     o.append("""Values are per dispatch, averaged over the run's dispatches of each kernel.  Derived columns:
 - MFMA busy = `SQ_VALU_MFMA_BUSY_CYCLES` / (`GRBM_GUI_ACTIVE` / 8 XCDs x 1024 SIMDs): the share of the
   kernel's wall cycles (at the clock it ran at) in which the matrix cores were busy.
