@@ -45,17 +45,20 @@ PEAK_HBM_GBS = 8000.0
 # HBM bytes per launch of the dominant kernel (the backward's dK/dV kernel on
 # the causal S=4096 workload), from rocprofv3 FETCH_SIZE and WRITE_SIZE runs
 # (profiles/bwd_causal_s4k_counters.md), each scaled by what the same counter
-# reads for a plain 1 GiB device copy; and the shader clock the kernel ran at
-# in those counter runs (GRBM_GUI_ACTIVE per XCD over the dispatch duration),
-# which prices the dense peak at the clock the power limit leaves.  Valid only
-# for the kernel sources whose digest is recorded here; reported as null once
-# they change.
+# reads for a plain 1 GiB device copy; and the wall cycles of one launch at the
+# shader clock in those counter runs (GRBM_GUI_ACTIVE per XCD, mean over the
+# passes that hold it).  A compute-bound kernel's cycle count holds while the
+# power limit moves its clock (the passes ran at 1.50-1.60 GHz within 0.7 % of
+# one count), so flops / (peak flops per cycle x cycles) is its fraction of the
+# dense peak at whatever clock it gets, and cycles / a live duration is the
+# clock of that live run.  Valid only for the kernel sources whose digest is
+# recorded here; reported as null once they change.
 TRAFFIC_SOURCES = ("exact_attention_128_amd/csrc/attn_bwd.hip",
                    "exact_attention_128_amd/csrc/gfx950.h",
                    "exact_attention_128_amd/csrc/attn_internal.h",
                    "exact_attention_128_amd/build.py")
 TRAFFIC = {"workload": "bwd_causal_s4k", "read_bytes": 229366563, "write_bytes": 67108864,
-           "clock_ghz": 1.924,
+           "cycles": 547409,
            "sources_sha256": "53d46275cb26cea5975d3e66432fbe296b0dfe8fbf3f39b86cf9decf60de397c"}
 # the same for the forward on the causal S=8192 workload
 # (profiles/fwd_causal_s8k_counters.md)
@@ -64,7 +67,7 @@ FWD_TRAFFIC_SOURCES = ("exact_attention_128_amd/csrc/attn_fwd.hip",
                        "exact_attention_128_amd/csrc/attn_internal.h",
                        "exact_attention_128_amd/build.py")
 FWD_TRAFFIC = {"workload": "fwd_causal_s8k", "read_bytes": 1383148222, "write_bytes": 136329493,
-               "clock_ghz": 1.542,
+               "cycles": 1750270,
                "sources_sha256": "f0d65c5b54bd6e2dcf5025f762d4e7f38e5c2372263b38846633ebbf538d3b16"}
 
 
@@ -90,14 +93,21 @@ def measured_traffic(workload, record=None, sources=None):
     return None if rec is None else rec["read_bytes"] + rec["write_bytes"]
 
 
-def at_profiled_clock(achieved, peak, workload, record=None, sources=None):
-    """(clock GHz, achieved / the dense peak at that clock) from the profiled
-    record, or (None, None)."""
+PEAK_BF16_FLOP_PER_CYCLE = 256 * 4096   # dense bf16 MFMA, whole chip, per shader clock
+
+
+def at_clock(flops, live_ms, workload, record=None, sources=None):
+    """From the profiled cycle count of one launch: {"cycles_profiled",
+    "frac_at_clock" = flops / (peak flops per cycle x cycles), the fraction of
+    the dense peak at the clock the kernel runs at, and "clock_ghz_live" =
+    cycles / the live duration}; all None without a valid record."""
     rec = measured_record(workload, record, sources)
-    if rec is None or "clock_ghz" not in rec:
-        return None, None
-    g = rec["clock_ghz"]
-    return g, round(achieved / (peak * g / 2.4), 4)
+    if rec is None or "cycles" not in rec:
+        return {"cycles_profiled": None, "frac_at_clock": None, "clock_ghz_live": None}
+    c = rec["cycles"]
+    return {"cycles_profiled": c,
+            "frac_at_clock": round(flops / (PEAK_BF16_FLOP_PER_CYCLE * c), 4),
+            "clock_ghz_live": round(c / (live_ms * 1e-3) / 1e9, 3)}
 
 
 def log(*a):
@@ -344,35 +354,38 @@ def pmc_summary(root, workload):
                      d["FETCH_SIZE"] * 1024 * fs / 1e6, mb(ar), d["WRITE_SIZE"] * 1024 * ws / 1e6,
                      mb(aw)))
     if clk:
-        o.append("\nMeasured clock.  Shader clock while profiled = `GRBM_GUI_ACTIVE` / 8 XCDs / the "
-                 "dispatch's duration (its start and end timestamps), averaged over the passes that "
-                 "hold the counter.  Dense peak at that clock = 2516.6 TFLOPS x clock / 2.4 GHz "
-                 "(FP8: twice).  Achieved = the kernel's credited algorithmic flops over the same "
-                 "mean duration:\n")
-        o.append("| Kernel | clock (GHz) | mean duration (us) | dense peak at that clock (TFLOPS) "
-                 "| achieved (TFLOPS) | fraction of the peak at that clock | fraction of the "
-                 "2.4 GHz peak |")
-        o.append("|---|---|---|---|---|---|---|")
+        o.append("\nMeasured clock.  Cycles per launch = `GRBM_GUI_ACTIVE` / 8 XCDs (wall cycles at "
+                 "the shader clock), clock = cycles / the dispatch's duration (its start and end "
+                 "timestamps), each the mean over the passes that hold the counter.  Fraction at "
+                 "the clock = the kernel's credited algorithmic flops / (256 CUs x 4096 bf16 flops "
+                 "per cycle, FP8 twice that, x cycles): its share of the dense peak at whatever "
+                 "clock it runs at.  Fraction of the 2.4 GHz peak = the same flops over the mean "
+                 "duration:\n")
+        o.append("| Kernel | cycles per launch | clock (GHz) | mean duration (us) | fraction at the "
+                 "clock | fraction of the 2.4 GHz peak |")
+        o.append("|---|---|---|---|---|---|")
         for k in order:
-            if k in clk:
-                g = sum(c for c, _ in clk[k]) / len(clk[k])
-                du = sum(t for _, t in clk[k]) / len(clk[k])
-                pk = (PEAK_FP8_TFLOPS if fam(k) == "attn_fwd_fp8_kernel" else PEAK_BF16_TFLOPS)
-                fl = None
-                if fam(k) in _CREDIT:
-                    kind, share = _CREDIT[fam(k)]
-                    fl = share * fwd_flops(w.B, w.H, w.S, w.D, w.causal) * (2.5 if kind == "bwd" else 1.0)
-                    if kind == "bwd" and not w.backward:
-                        fl = None
-                    if kind == "fwd" and w.backward and fam(k) == "attn_fwd_kernel":
-                        fl = fwd_flops(w.B, w.H, w.S, w.D, w.causal)
-                if fl is None:
-                    o.append("| `%s` | %.3f | %.1f | %.1f | - | - | - |" % (short(k), g, du / 1e3,
-                                                                             pk * g / 2.4))
+            if k not in clk:
+                continue
+            cyc = sum(c * t for c, t in clk[k]) / len(clk[k])
+            g = sum(c for c, _ in clk[k]) / len(clk[k])
+            du = sum(t for _, t in clk[k]) / len(clk[k])
+            per_cycle = PEAK_BF16_FLOP_PER_CYCLE * (2 if fam(k) == "attn_fwd_fp8_kernel" else 1)
+            pk = PEAK_FP8_TFLOPS if fam(k) == "attn_fwd_fp8_kernel" else PEAK_BF16_TFLOPS
+            fl = None
+            if fam(k) in _CREDIT:
+                kind, share = _CREDIT[fam(k)]
+                if kind == "bwd":
+                    fl = (share * 2.5 * fwd_flops(w.B, w.H, w.S, w.D, w.causal)
+                          if w.backward else None)
                 else:
-                    t = fl / (du * 1e-9) / 1e12
-                    o.append("| `%s` | %.3f | %.1f | %.1f | %.1f | %.4f | %.4f |" % (
-                        short(k), g, du / 1e3, pk * g / 2.4, t, t / (pk * g / 2.4), t / pk))
+                    fl = fwd_flops(w.B, w.H, w.S, w.D, w.causal)
+            if fl is None:
+                o.append("| `%s` | %d | %.3f | %.1f | - | - |" % (short(k), round(cyc), g, du / 1e3))
+            else:
+                o.append("| `%s` | %d | %.3f | %.1f | %.4f | %.4f |" % (
+                    short(k), round(cyc), g, du / 1e3, fl / (per_cycle * cyc),
+                    fl / (du * 1e-9) / 1e12 / pk))
     o.append("\nHBM bytes per launch (scaled): " + "; ".join(
         "`%s` read %d, write %d" % (fam(k), round(raw[k]["FETCH_SIZE"] * 1024 * fs),
                                     round(raw[k]["WRITE_SIZE"] * 1024 * ws)) for k in order) + "\n")
@@ -712,8 +725,9 @@ def main():
                     "median_ms": c3["median_ms"], "frac_median": c3["frac_peak_median"],
                     "frac_vs_library_gemm": round(c3["tflops"] / gemm_tflops, 4),
                     "traffic": measured_traffic("fwd_causal_s8k", FWD_TRAFFIC, FWD_TRAFFIC_SOURCES)}
-        fwd_roof["clock_ghz_profiled"], fwd_roof["frac_at_profiled_clock"] = at_profiled_clock(
-            c3["tflops"], PEAK_BF16_TFLOPS, "fwd_causal_s8k", FWD_TRAFFIC, FWD_TRAFFIC_SOURCES)
+        cw = ai.WORKLOADS["fwd_causal_s8k"]
+        fwd_roof.update(at_clock(fwd_flops(cw.B, cw.H, cw.S, cw.D, cw.causal), c3["ms"],
+                                 "fwd_causal_s8k", FWD_TRAFFIC, FWD_TRAFFIC_SOURCES))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -733,7 +747,7 @@ def main():
                "per_config": cpu_legs}
         log("cpu oracle: %s" % cpu)
 
-    main_clk = at_profiled_clock(main_tflops, PEAK_BF16_TFLOPS, w.name)
+    main_clk = at_clock(0.8 * f_bwd, ms_main, w.name)
     out = {
         "metric": "attention fwd/bwd TFLOPS (bf16, D=128) and % of MI355X bf16 MFMA peak",
         "value": round(value, 2),
@@ -758,7 +772,7 @@ def main():
                                           PEAK_BF16_TFLOPS, 4),
                      "frac_vs_library_gemm": (round(main_tflops / gemm_tflops, 4)
                                               if gemm_tflops else None),
-                     "clock_ghz_profiled": main_clk[0], "frac_at_profiled_clock": main_clk[1]},
+                     **main_clk},
         "dq_kernel": {"kernel": "attn_bwd_dq_kernel<128,causal>", "ms": round(ms_dq, 4),
                       "median_ms": round(med_dq, 4),
                       "algorithmic_tflops": round(dq_alg_tflops, 1),

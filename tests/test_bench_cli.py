@@ -135,17 +135,19 @@ def test_pmc_summary_scales_bytes_by_the_copy(tmp_path):
     assert "read %d, write %d" % (1000 * 1024 * 2, 3000 * 1024) in md
 
 
-def test_clock_record_prices_the_peak_at_that_clock(tmp_path):
-    """at_profiled_clock divides the achieved rate by the dense peak scaled to
-    the recorded clock, and gives nothing once the sources change."""
+def test_cycle_record_gives_the_fraction_at_the_clock(tmp_path):
+    """at_clock: flops over (peak flops per cycle x profiled cycles), the live
+    clock as cycles over the live duration, and nothing once the sources
+    change."""
     import hashlib
     b = _bench()
     src = tmp_path / "k.hip"
     src.write_bytes(b"v1")
     rel = os.path.relpath(str(src), ROOT)
-    rec = {"workload": "w", "read_bytes": 1, "write_bytes": 1, "clock_ghz": 1.2,
+    rec = {"workload": "w", "read_bytes": 1, "write_bytes": 1, "cycles": 1_000_000,
            "sources_sha256": hashlib.sha256(b"v1").hexdigest()}
-    g, frac = b.at_profiled_clock(629.15, 2516.6, "w", rec, (rel,))
-    assert g == 1.2 and frac == 0.5
+    flops = 0.5 * 256 * 4096 * 1_000_000
+    r = b.at_clock(flops, 0.625, "w", rec, (rel,))
+    assert r == {"cycles_profiled": 1_000_000, "frac_at_clock": 0.5, "clock_ghz_live": 1.6}
     src.write_bytes(b"v2")
-    assert b.at_profiled_clock(629.15, 2516.6, "w", rec, (rel,)) == (None, None)
+    assert b.at_clock(flops, 0.625, "w", rec, (rel,))["frac_at_clock"] is None
