@@ -69,6 +69,17 @@ FWD_TRAFFIC_SOURCES = ("exact_attention_128_amd/csrc/attn_fwd.hip",
 FWD_TRAFFIC = {"workload": "fwd_causal_s8k", "read_bytes": 1383148222, "write_bytes": 136329493,
                "cycles": 1750270,
                "sources_sha256": "f0d65c5b54bd6e2dcf5025f762d4e7f38e5c2372263b38846633ebbf538d3b16"}
+# the wall cycles of the step's three kernels on the causal S=4096 workload
+# (forward, dQ, dK/dV; profiles/bwd_causal_s4k_counters.md): the step's work
+# per cycle, whatever clock the power limit leaves it
+STEP_SOURCES = ("exact_attention_128_amd/csrc/attn_fwd.hip",
+                "exact_attention_128_amd/csrc/attn_bwd.hip",
+                "exact_attention_128_amd/csrc/attn_bwd_dq.hip",
+                "exact_attention_128_amd/csrc/gfx950.h",
+                "exact_attention_128_amd/csrc/attn_internal.h",
+                "exact_attention_128_amd/build.py")
+STEP_CYCLES = {"workload": "bwd_causal_s4k", "cycles": 284551 + 355738 + 547409,
+               "sources_sha256": "4c31329a4bca1d9343c8792da05e89372fad43419eafdacb3ce6da0062e31c0d"}
 
 
 def measured_record(workload, record=None, sources=None):
@@ -779,6 +790,7 @@ def main():
                       "executed_tflops": round(dq_exec_tflops, 1),
                       "executed_frac": round(dq_exec_tflops / PEAK_BF16_TFLOPS, 4)},
         "ms_per_step_median": round(ms_step_median, 4),
+        "step_at_clock": at_clock(f_fwd + f_bwd, ms_step, w.name, STEP_CYCLES, STEP_SOURCES),
         "fwd_ms": round(ms_fwd, 4),
         "fwd_median_ms": round(med_fwd, 4),
         "bwd_ms": round(ms_bwd, 4),
