@@ -9,9 +9,10 @@ that exercises every step.  Throughput is algorithmic TFLOPS: forward
 4*B*H*S^2*D (halved when causal) plus backward 2.5x that.
 
 Also measured, in the same process:
-  * the dominant kernel (the backward's dK/dV kernel) on its own, timed with
-    HIP events on the stream it is launched on -> "roofline" (MFMA bound); the
-    backward's dQ kernel likewise -> "dq_kernel";
+  * the dominant kernel (the backward's dK/dV kernel), timed with HIP events
+    on the stream it is launched on, in the same K steps run once more with an
+    event between the step's kernels -> "roofline" (MFMA bound); the backward's
+    dQ kernel likewise -> "dq_kernel" (each also timed alone, "alone_ms");
   * the forward alone on the four forward workloads (S=128 D=64 non-causal, a
     latency case reported with its algorithmic HBM rate; S=2048 non-causal;
     S=8192 causal; S=16384 causal rising-maximum) -> "legs" and "fwd_roofline";
@@ -408,6 +409,47 @@ def pmc_summary(root, workload):
     return "\n".join(o)
 
 
+def lap_windows(path, steps, warmup):
+    """The trace's durations over exactly the launches bench.py's live timing
+    covers, for the two roofline kernels (a bench run traced with the same
+    --steps and --warmup): the dK/dV kernel's steps-long instrumented step loop
+    comes after its warmup + steps launches of the timed step loop; the causal
+    S=8192 forward's leg laps after three warm-up launches and one warm launch.
+    Returns markdown lines (trace mean and start-to-start mean per window)."""
+    import csv
+    import statistics
+    import attn_inputs as ai
+    n_rep = max(steps, 10)
+    wb, wf = ai.WORKLOADS["bwd_causal_s4k"], ai.WORKLOADS["fwd_causal_s8k"]
+    spans = {("attn_bwd_main_kernel", _grids(wb)["attn_bwd_main_kernel"]): (warmup + steps, steps,
+                                                                           False),
+             ("attn_fwd_kernel", _grids(wf)["attn_fwd_kernel"]): (4, n_rep, True)}
+    runs = {k: [] for k in spans}
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            name = r["Kernel_Name"]
+            fam = name.split("<")[0].split("::")[-1].strip()
+            targs = name.split("<")[1].split(">")[0].split(",") if "<" in name else []
+            if len(targs) > 2 and targs[2].strip() == "true":
+                continue   # the counting instantiation
+            key = (fam, int(r["Grid_Size_X"]))
+            if key in runs and targs[1].strip() == "true":
+                runs[key].append((int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    out = []
+    for (fam, grid), (first, n, back_to_back) in spans.items():
+        t = sorted(runs[(fam, grid)])[first:first + n]
+        if len(t) < 2:
+            continue
+        dur = [(e - b) / 1e3 for b, e in t]
+        line = "- `%s` (grid %d), launches %d..%d in trace order: mean %.1f us, median %.1f us" % (
+            fam, grid, first + 1, first + len(t), statistics.mean(dur), statistics.median(dur))
+        if back_to_back:
+            gap = [(t[i + 1][0] - t[i][0]) / 1e3 for i in range(len(t) - 1)]
+            line += ", start-to-start %.1f us" % statistics.mean(gap)
+        out.append(line)
+    return out
+
+
 SWEEP_TAUS = (0.0, 8.0, 16.0, 32.0, 64.0)
 SWEEP_POLYS = (0, 8, 4)
 
@@ -503,6 +545,9 @@ def main():
         return
     if args.trace_summary is not None:
         print(trace_summary(args.trace_summary))
+        print("\nThe launches the live laps time (this run's --steps %d --warmup %d):\n" % (
+            args.steps, args.warmup))
+        print("\n".join(lap_windows(args.trace_summary, args.steps, args.warmup)))
         return
     if args.pmc_summary is not None:
         print(pmc_summary(*args.pmc_summary))
@@ -560,6 +605,32 @@ def main():
     log("step: %.3f ms  %.1f TFLOPS (wall %.3f ms/step)" % (ms_step, value,
                                                           1e3 * t_wall / args.steps))
 
+    # The same K steps once more with an event between the step's kernels
+    # (forward | dQ and row statistics | dK/dV, the backward split into its two
+    # launches, the same GPU work): each kernel's duration in the step, where
+    # it shares the clock with the other two.  Each event marker costs a few
+    # microseconds of idle time, which is why the step itself is timed above
+    # without them.
+    kev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * args.steps + 1)]
+    kev[0].record(stream)
+    for i in range(args.steps):
+        A.fwd_out(q, k, v, o, lse, causal=causal, scale=scale)
+        kev[3 * i + 1].record(stream)
+        A.bwd_out(q, k, v, o, lse, do, dq, dk, dv, ws, causal=causal, scale=scale,
+                  phases=A.BWD_DQ)
+        kev[3 * i + 2].record(stream)
+        A.bwd_out(q, k, v, o, lse, do, dq, dk, dv, ws, causal=causal, scale=scale,
+                  phases=A.BWD_MAIN)
+        kev[3 * i + 3].record(stream)
+    torch.cuda.synchronize()
+    in_step = {n: [kev[3 * i + j].elapsed_time(kev[3 * i + j + 1]) for i in range(args.steps)]
+               for j, n in enumerate(("fwd", "dq", "main"))}
+    ms_main = float(np.mean(in_step["main"]))
+    med_main = float(np.median(in_step["main"]))
+    ms_dq = float(np.mean(in_step["dq"]))
+    med_dq = float(np.median(in_step["dq"]))
+    ms_fwd_step = float(np.mean(in_step["fwd"]))
+
     def time_launches(fn, n):
         """Mean launch time in ms over n back-to-back launches (HIP events on the
         launch stream); the per-launch times go to `laps` for the median."""
@@ -585,14 +656,16 @@ def main():
     # backward's five products (S, dP, dV, dK): 0.8 of the backward FLOPs.  The
     # dQ kernel's algorithmic work is the fifth (dQ); it also recomputes S and
     # dP, which the count leaves out.
+    # Also each kernel alone, back to back (context: a lone run of the heaviest
+    # kernel holds the clock lower than the mixed step does).
     A.bwd_out(q, k, v, o, lse, do, dq, dk, dv, ws, causal=causal, scale=scale, phases=A.BWD_PRE)
     n_rep = max(args.steps, 10)
-    ms_main = time_launches(lambda: A.bwd_out(q, k, v, o, lse, do, dq, dk, dv, ws, causal=causal,
-                                              scale=scale, phases=A.BWD_MAIN), n_rep)
-    med_main = last_median()
-    ms_dq = time_launches(lambda: A.bwd_out(q, k, v, o, lse, do, dq, dk, dv, ws, causal=causal,
-                                            scale=scale, phases=A.BWD_DQ), n_rep)
-    med_dq = last_median()
+    ms_main_alone = time_launches(lambda: A.bwd_out(q, k, v, o, lse, do, dq, dk, dv, ws,
+                                                    causal=causal, scale=scale,
+                                                    phases=A.BWD_MAIN), n_rep)
+    ms_dq_alone = time_launches(lambda: A.bwd_out(q, k, v, o, lse, do, dq, dk, dv, ws,
+                                                  causal=causal, scale=scale, phases=A.BWD_DQ),
+                                n_rep)
     ms_fwd = time_launches(lambda: A.fwd_out(q, k, v, o, lse, causal=causal, scale=scale), n_rep)
     med_fwd = last_median()
     ms_bwd = time_launches(lambda: A.bwd_out(q, k, v, o, lse, do, dq, dk, dv, ws, causal=causal,
@@ -601,8 +674,10 @@ def main():
     main_tflops = 0.8 * f_bwd / (ms_main * 1e-3) / 1e12
     dq_alg_tflops = 0.2 * f_bwd / (ms_dq * 1e-3) / 1e12
     dq_exec_tflops = 0.6 * f_bwd / (ms_dq * 1e-3) / 1e12
-    log("bwd dK/dV %.3f ms (%.1f TFLOPS), dQ %.3f ms (%.1f executed TFLOPS), fwd %.3f ms, "
-        "bwd total %.3f ms" % (ms_main, main_tflops, ms_dq, dq_exec_tflops, ms_fwd, ms_bwd))
+    log("in the step: dK/dV %.3f ms (%.1f TFLOPS), dQ %.3f ms (%.1f executed TFLOPS), fwd %.3f ms"
+        % (ms_main, main_tflops, ms_dq, dq_exec_tflops, ms_fwd_step))
+    log("alone: dK/dV %.3f ms, dQ %.3f ms, fwd %.3f ms, bwd total %.3f ms" % (
+        ms_main_alone, ms_dq_alone, ms_fwd, ms_bwd))
 
     legs = {}
     cpu_legs = {}
@@ -783,9 +858,11 @@ def main():
                                           PEAK_BF16_TFLOPS, 4),
                      "frac_vs_library_gemm": (round(main_tflops / gemm_tflops, 4)
                                               if gemm_tflops else None),
+                     "timed": "in the step, %d steps" % args.steps,
+                     "alone_ms": round(ms_main_alone, 4),
                      **main_clk},
         "dq_kernel": {"kernel": "attn_bwd_dq_kernel<128,causal>", "ms": round(ms_dq, 4),
-                      "median_ms": round(med_dq, 4),
+                      "median_ms": round(med_dq, 4), "alone_ms": round(ms_dq_alone, 4),
                       "algorithmic_tflops": round(dq_alg_tflops, 1),
                       "executed_tflops": round(dq_exec_tflops, 1),
                       "executed_frac": round(dq_exec_tflops / PEAK_BF16_TFLOPS, 4)},
