@@ -58,18 +58,18 @@ TRAFFIC_SOURCES = ("exact_attention_128_amd/csrc/attn_bwd.hip",
                    "exact_attention_128_amd/csrc/gfx950.h",
                    "exact_attention_128_amd/csrc/attn_internal.h",
                    "exact_attention_128_amd/build.py")
-TRAFFIC = {"workload": "bwd_causal_s4k", "read_bytes": 229366563, "write_bytes": 67108864,
-           "cycles": 547409,
-           "sources_sha256": "53d46275cb26cea5975d3e66432fbe296b0dfe8fbf3f39b86cf9decf60de397c"}
+TRAFFIC = {"workload": "bwd_causal_s4k", "read_bytes": 229256980, "write_bytes": 67108864,
+           "cycles": 544475,
+           "sources_sha256": "690239f7a2c3b690ce3c243c4442d8b1828f9809b648a7cb82a19b8585b142e1"}
 # the same for the forward on the causal S=8192 workload
 # (profiles/fwd_causal_s8k_counters.md)
 FWD_TRAFFIC_SOURCES = ("exact_attention_128_amd/csrc/attn_fwd.hip",
                        "exact_attention_128_amd/csrc/gfx950.h",
                        "exact_attention_128_amd/csrc/attn_internal.h",
                        "exact_attention_128_amd/build.py")
-FWD_TRAFFIC = {"workload": "fwd_causal_s8k", "read_bytes": 1383148222, "write_bytes": 136329493,
-               "cycles": 1750270,
-               "sources_sha256": "f0d65c5b54bd6e2dcf5025f762d4e7f38e5c2372263b38846633ebbf538d3b16"}
+FWD_TRAFFIC = {"workload": "fwd_causal_s8k", "read_bytes": 586612928, "write_bytes": 136314880,
+               "cycles": 1767422,
+               "sources_sha256": "c41d07edcedf08c129d7a9f602bbd6fafa9ad33ad6a4178dabb58a95d60c6831"}
 # the wall cycles of the step's three kernels on the causal S=4096 workload
 # (forward, dQ, dK/dV; profiles/bwd_causal_s4k_counters.md): the step's work
 # per cycle, whatever clock the power limit leaves it
@@ -79,8 +79,8 @@ STEP_SOURCES = ("exact_attention_128_amd/csrc/attn_fwd.hip",
                 "exact_attention_128_amd/csrc/gfx950.h",
                 "exact_attention_128_amd/csrc/attn_internal.h",
                 "exact_attention_128_amd/build.py")
-STEP_CYCLES = {"workload": "bwd_causal_s4k", "cycles": 284551 + 355738 + 547409,
-               "sources_sha256": "4c31329a4bca1d9343c8792da05e89372fad43419eafdacb3ce6da0062e31c0d"}
+STEP_CYCLES = {"workload": "bwd_causal_s4k", "cycles": 279140 + 345687 + 544475,
+               "sources_sha256": "c625de70ba0cba454599d840d19e3ade0626b53867b39585700dce8bc8b0b87d"}
 
 
 def measured_record(workload, record=None, sources=None):

@@ -25,6 +25,8 @@ struct FwdParams {
   float tau;      // rescale threshold in log2 units
   float thresh;   // 2^tau: a lane's partial weight sum above it triggers a rescale
   int xcd_heads;  // heads per XCD for the XCD-aware block order, 0 = plain order
+  int xcd_group;  // causal: an XCD works through its heads this many at a time
+                  // (divides xcd_heads; = xcd_heads: all at once)
   unsigned long long* events;  // diagnostic counters (see attn_fwd_rescale_events), or null
 };
 
