@@ -48,28 +48,28 @@ PEAK_HBM_GBS = 8000.0
 # (profiles/bwd_causal_s4k_counters.md), each scaled by what the same counter
 # reads for a plain 1 GiB device copy; and the wall cycles of one launch at the
 # shader clock in those counter runs (GRBM_GUI_ACTIVE per XCD, mean over the
-# passes that hold it).  A compute-bound kernel's cycle count holds while the
-# power limit moves its clock (the passes ran at 1.50-1.60 GHz within 0.7 % of
-# one count), so flops / (peak flops per cycle x cycles) is its fraction of the
-# dense peak at whatever clock it gets, and cycles / a live duration is the
-# clock of that live run.  Valid only for the kernel sources whose digest is
+# passes that hold it).  A compute-bound kernel's cycle count holds far better
+# than its clock under the power limit (one run's passes at 1.50-1.60 GHz agree
+# to 0.7 %; runs on different boxes to about 3 %), so flops / (peak flops per
+# cycle x cycles) is its fraction of the dense peak at the clock it gets, and
+# cycles / a live duration estimates the clock of that live run.  Valid only for the kernel sources whose digest is
 # recorded here; reported as null once they change.
 TRAFFIC_SOURCES = ("exact_attention_128_amd/csrc/attn_bwd.hip",
                    "exact_attention_128_amd/csrc/gfx950.h",
                    "exact_attention_128_amd/csrc/attn_internal.h",
                    "exact_attention_128_amd/build.py")
-TRAFFIC = {"workload": "bwd_causal_s4k", "read_bytes": 229256980, "write_bytes": 67108864,
-           "cycles": 544475,
-           "sources_sha256": "690239f7a2c3b690ce3c243c4442d8b1828f9809b648a7cb82a19b8585b142e1"}
+TRAFFIC = {"workload": "bwd_causal_s4k", "read_bytes": 229495376, "write_bytes": 67108864,
+           "cycles": 555846,
+           "sources_sha256": "7fe307eae0ad79c42b154025b69cc8375307c9cbfc87575f071fa78c249af9f3"}
 # the same for the forward on the causal S=8192 workload
 # (profiles/fwd_causal_s8k_counters.md)
 FWD_TRAFFIC_SOURCES = ("exact_attention_128_amd/csrc/attn_fwd.hip",
                        "exact_attention_128_amd/csrc/gfx950.h",
                        "exact_attention_128_amd/csrc/attn_internal.h",
                        "exact_attention_128_amd/build.py")
-FWD_TRAFFIC = {"workload": "fwd_causal_s8k", "read_bytes": 586612928, "write_bytes": 136314880,
-               "cycles": 1767422,
-               "sources_sha256": "c41d07edcedf08c129d7a9f602bbd6fafa9ad33ad6a4178dabb58a95d60c6831"}
+FWD_TRAFFIC = {"workload": "fwd_causal_s8k", "read_bytes": 585427804, "write_bytes": 136314880,
+               "cycles": 1815851,
+               "sources_sha256": "f773dacc78f18650f38c03dfffde94fa1d60160aff96111243cfeafa4b7d5ab4"}
 # the wall cycles of the step's three kernels on the causal S=4096 workload
 # (forward, dQ, dK/dV; profiles/bwd_causal_s4k_counters.md): the step's work
 # per cycle, whatever clock the power limit leaves it
@@ -79,8 +79,8 @@ STEP_SOURCES = ("exact_attention_128_amd/csrc/attn_fwd.hip",
                 "exact_attention_128_amd/csrc/gfx950.h",
                 "exact_attention_128_amd/csrc/attn_internal.h",
                 "exact_attention_128_amd/build.py")
-STEP_CYCLES = {"workload": "bwd_causal_s4k", "cycles": 279140 + 345687 + 544475,
-               "sources_sha256": "c625de70ba0cba454599d840d19e3ade0626b53867b39585700dce8bc8b0b87d"}
+STEP_CYCLES = {"workload": "bwd_causal_s4k", "cycles": 290566 + 364283 + 555846,
+               "sources_sha256": "b6b9e928bfb0065dc4ddd12cd276d6f7a9c56b023ceb38da545e0bcb38e7cdc0"}
 
 
 def measured_record(workload, record=None, sources=None):

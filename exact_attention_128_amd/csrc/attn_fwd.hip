@@ -564,28 +564,13 @@ void attn_fwd_kernel(FwdParams p) {
   }
 }
 
-// Causal XCD order: how many of an XCD's heads it works on at a time.  The
-// largest divisor of the XCD's head count whose K/V (2*S*D bf16 per head)
-// stays within 8 MiB, two L2s' worth, but at least two heads: with one head at
-// a time the heaviest blocks of each head start late and the tail grows
-// (measured: +28 % on 32 heads of S = 4096).  Measured on 64 heads of S = 8192
-// (4 MiB each, groups of 2 against all 8 of an XCD's heads at once): -1.6 to
-// -2.2 % time, the same bits.
-static int xcd_group(int hpx, int S, int D) {
-  if (hpx <= 2) return hpx > 0 ? hpx : 1;
-  const long per_head = 4L * S * D;
-  int g = hpx;
-  while (g > 2 && (g * per_head > (8L << 20) || hpx % g != 0)) --g;
-  return hpx % g == 0 ? g : hpx;
-}
-
 template <int D, bool CAUSAL, bool COUNT = false, int POLY = 0>
 static hipError_t launch_fwd_t(const FwdParams& p0, hipStream_t stream) {
   constexpr int NW = 8;
   FwdParams p = p0;
   p.nqb = (p.S + 32 * NW - 1) / (32 * NW);
   p.xcd_heads = (p.bh % 8 == 0) ? p.bh / 8 : 0;
-  p.xcd_group = xcd_group(p.xcd_heads, p.S, D);
+  p.xcd_group = xcd_group(p.xcd_heads, 4L * p.S * D);   // bf16 K and V of a head
   p.thresh = exp2f(p.tau);
   const long grid = (long)p.bh * p.nqb;
   if (grid <= 0 || grid * NW * 64 > 0xffffffffL) return hipErrorInvalidConfiguration;

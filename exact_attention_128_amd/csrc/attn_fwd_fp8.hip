@@ -136,10 +136,12 @@ void attn_fwd_fp8_kernel(Fp8FwdParams p) {
   {
     const int u = blockIdx.x;
     if (p.xcd_heads > 0) {
-      const int x = u & 7, j = u >> 3, hpx = p.xcd_heads;
+      const int x = u & 7, j = u >> 3;
       if (CAUSAL) {
-        qi = j / hpx;
-        bh = x + 8 * (j % hpx);
+        // the XCD's heads a group at a time, heaviest block first within it
+        const int G = p.xcd_group, per = G * p.nqb, gi = j / per, r = j % per;
+        qi = r / G;
+        bh = x + 8 * (gi * G + r % G);
       } else {
         bh = x + 8 * (j / p.nqb);
         qi = j % p.nqb;
@@ -480,6 +482,7 @@ static hipError_t launch_fp8_t(const Fp8FwdParams& p0, hipStream_t stream) {
   Fp8FwdParams p = p0;
   p.nqb = (p.S + 32 * NW - 1) / (32 * NW);
   p.xcd_heads = (p.bh % 8 == 0) ? p.bh / 8 : 0;
+  p.xcd_group = xcd_group(p.xcd_heads, 2L * p.S * D);   // E4M3 K and V of a head
   const long grid = (long)p.bh * p.nqb;
   if (grid <= 0 || grid * NW * 64 > 0xffffffffL) return hipErrorInvalidConfiguration;
   void* args[] = {&p};
