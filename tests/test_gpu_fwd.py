@@ -109,6 +109,28 @@ def test_many_units(shape, causal):
     P.assert_fwd_ok(err, "persistent %s causal=%s" % (shape, causal))
 
 
+@pytest.mark.parametrize("shape", [(1, 48, 4096, 128), (1, 72, 4096, 128), (1, 64, 8192, 64)])
+def test_causal_head_groups(shape):
+    """The causal XCD order in K/V-sized head groups: 6 heads per XCD in
+    groups of 3 (S = 4096, 2 MiB of K/V per head), 9 per XCD with no divisor
+    that fits (all at once), 8 per XCD in groups of 4 at D = 64.  One row of
+    every 256-row query block of every head, plus the block edges, against
+    the oracle, so a block computed twice, never, or for the wrong head
+    shows."""
+    B, H, S, D = shape
+    bits = ai.make_inputs(B, H, S, D, 4100 + H + D)
+    scale = 1.0 / np.sqrt(D)
+    o, lse, _ = P.gpu_fwd(bits, True, scale)
+    rows = {}
+    for hd in range(B * H):
+        r = {0, 255, 256, S // 2, S - 1}
+        r.update(256 * b + (37 * b + 11 * hd) % 256 for b in range(S // 256))
+        rows[hd] = np.array(sorted(r), dtype=np.int64)
+    err = P.sampled_fwd_errors(o, lse, bits, True, scale, rows)
+    print(shape, err)
+    P.assert_fwd_ok(err, "head groups %s" % (shape,))
+
+
 @pytest.mark.parametrize("scale", [1.0, -0.09, 0.0, 0.5, 16.0])
 def test_scale_values(scale):
     """Off-standard scales, up to 16 (scores of a few hundred, rows dominated by
