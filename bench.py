@@ -2,11 +2,12 @@
 """Benchmark of the fused exact-attention hot path on one MI355X.
 
 One step = the whole path over one batch of seeded synthetic input: the fused
-forward (O, LSE) followed by the backward (row statistics, dK/dV, dQ) that
-consumes the forward's O and LSE.  The default workload is the
+forward (O, LSE) followed by the backward (dQ with the row statistics, then
+dK/dV) that consumes the forward's O and LSE.  The default workload is the
 causal backward workload (B=2, H=16, S=4096, D=128, bf16), the one workload
 that exercises every step.  Throughput is algorithmic TFLOPS: forward
-4*B*H*S^2*D (halved when causal) plus backward 2.5x that.
+4*B*H*S^2*D (halved when causal) plus backward 2.5x that, over K timed steps
+after W warm-up steps (defaults 100 and 30: the clock settles first).
 
 Also measured, in the same process:
   * the dominant kernel (the backward's dK/dV kernel), timed with HIP events
@@ -22,6 +23,12 @@ Also measured, in the same process:
   * the FP8 (E4M3) forward on the S=8192 causal shape against the FP8 peak;
   * calibration legs that are not on the path: a library bf16 GEMM (what the
     matrix cores sustain) and a 1 GiB device copy (what HBM sustains);
+  * the forward and the whole backward each alone, back to back -> "fwd_ms",
+    "bwd_ms";
+  * from rocprofv3 records of the same kernel sources (reported only while
+    the sources' digest matches): HBM bytes per launch -> "traffic", and wall
+    cycles per launch -> "cycles_profiled", "frac_at_clock" (work per cycle
+    against the peak's) and "step_at_clock" for the whole step;
   * the fp64 CPU oracle on a bounded sample of the same workload on this host's
     cores -> "cpu_baseline" (a reported baseline, not the target).
 
