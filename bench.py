@@ -653,9 +653,17 @@ def main():
     ms_fwd_step = float(np.mean(in_step["fwd"]))
 
     def time_launches(fn, n):
-        """Mean launch time in ms over n back-to-back launches (HIP events on the
-        launch stream); the per-launch times go to `laps` for the median."""
+        """Mean launch time in ms over n back-to-back launches between two HIP
+        events on the launch stream (an event after each launch would add its
+        marker's few microseconds to every launch); the per-launch times of n
+        more launches, an event after each, go to `laps` for the median."""
         fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(n):
+            fn()
+        b.record(stream)
         torch.cuda.synchronize()
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
         ev[0].record(stream)
@@ -663,9 +671,8 @@ def main():
             fn()
             ev[i + 1].record(stream)
         torch.cuda.synchronize()
-        t = [ev[i].elapsed_time(ev[i + 1]) for i in range(n)]
-        laps.append(t)
-        return ev[0].elapsed_time(ev[n]) / n
+        laps.append([ev[i].elapsed_time(ev[i + 1]) for i in range(n)])
+        return a.elapsed_time(b) / n
 
     laps = []
 
