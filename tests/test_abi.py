@@ -55,6 +55,33 @@ def _fwd(lib, q=P, k=P, v=P, o=P, lse=P, B=1, H=1, S=16, D=128, scale=0.1, causa
     return lib.attn_fwd(q, k, v, o, lse, B, H, S, D, scale, causal, None)
 
 
+def _fp8(lib, q=P, k=P, v=P, o=P, lse=P, B=1, H=1, S=16, D=128, scale=0.1, causal=0,
+         qd=1.0, kd=1.0, vd=1.0):
+    return lib.attn_fwd_fp8(q, k, v, o, lse, B, H, S, D, scale, causal, qd, kd, vd, None)
+
+
+def test_fp8_validation(lib):
+    """attn_fwd_fp8 rejects every bad request on the host, before any HIP call."""
+    nan, inf = float("nan"), float("inf")
+    assert _fp8(lib, k=None) == 1
+    assert _fp8(lib, lse=None) == 1
+    assert _fp8(lib, S=0) == 2
+    assert _fp8(lib, B=1 << 20, H=1 << 10, S=1 << 10) == 2
+    assert _fp8(lib, D=96) == 3
+    assert _fp8(lib, q=P + 8) == 4
+    assert _fp8(lib, o=P + 2) == 4
+    assert _fp8(lib, lse=P + 2) == 4
+    for d in (0.0, -1.0, nan, inf):
+        assert _fp8(lib, qd=d) == 6
+        assert _fp8(lib, kd=d) == 6
+        assert _fp8(lib, vd=d) == 6
+    assert _fp8(lib, scale=nan) == 6
+    # the scale reaching the scores is scale * q_descale * k_descale: finite
+    # factors whose product overflows fp32 after the log2(e) factor are refused
+    assert _fp8(lib, scale=1e30, qd=1e10) == 6
+    assert _fp8(lib, scale=2.4e38) == 6   # 2.4e38 * log2(e) > FLT_MAX
+
+
 def test_fwd_validation(lib):
     assert _fwd(lib, q=None) == 1
     assert _fwd(lib, lse=None) == 1
