@@ -65,18 +65,18 @@ TRAFFIC_SOURCES = ("exact_attention_128_amd/csrc/attn_bwd.hip",
                    "exact_attention_128_amd/csrc/gfx950.h",
                    "exact_attention_128_amd/csrc/attn_internal.h",
                    "exact_attention_128_amd/build.py")
-TRAFFIC = {"workload": "bwd_causal_s4k", "read_bytes": 229495376, "write_bytes": 67108864,
-           "cycles": 555846,
-           "sources_sha256": "7fe307eae0ad79c42b154025b69cc8375307c9cbfc87575f071fa78c249af9f3"}
+TRAFFIC = {"workload": "bwd_causal_s4k", "read_bytes": 231122800, "write_bytes": 67108864,
+           "cycles": 513420,
+           "sources_sha256": "f5c3e9878cf68e6bffb25d140d34738ec91b7e2b4844818e28f81b540d4e5c96"}
 # the same for the forward on the causal S=8192 workload
 # (profiles/fwd_causal_s8k_counters.md)
 FWD_TRAFFIC_SOURCES = ("exact_attention_128_amd/csrc/attn_fwd.hip",
                        "exact_attention_128_amd/csrc/gfx950.h",
                        "exact_attention_128_amd/csrc/attn_internal.h",
                        "exact_attention_128_amd/build.py")
-FWD_TRAFFIC = {"workload": "fwd_causal_s8k", "read_bytes": 585427804, "write_bytes": 136314880,
-               "cycles": 1815851,
-               "sources_sha256": "f773dacc78f18650f38c03dfffde94fa1d60160aff96111243cfeafa4b7d5ab4"}
+FWD_TRAFFIC = {"workload": "fwd_causal_s8k", "read_bytes": 582236146, "write_bytes": 136314880,
+               "cycles": 1785060,
+               "sources_sha256": "412e51c456aef46b77c96fbc56224be43a66320f04cbf535c1603f18e24d3cc1"}
 # the wall cycles of the step's three kernels on the causal S=4096 workload
 # (forward, dQ, dK/dV; profiles/bwd_causal_s4k_counters.md): the step's work
 # per cycle, whatever clock the power limit leaves it
@@ -86,8 +86,8 @@ STEP_SOURCES = ("exact_attention_128_amd/csrc/attn_fwd.hip",
                 "exact_attention_128_amd/csrc/gfx950.h",
                 "exact_attention_128_amd/csrc/attn_internal.h",
                 "exact_attention_128_amd/build.py")
-STEP_CYCLES = {"workload": "bwd_causal_s4k", "cycles": 290566 + 364283 + 555846,
-               "sources_sha256": "b6b9e928bfb0065dc4ddd12cd276d6f7a9c56b023ceb38da545e0bcb38e7cdc0"}
+STEP_CYCLES = {"workload": "bwd_causal_s4k", "cycles": 284524 + 349565 + 513420,
+               "sources_sha256": "d0522020f0e5917d7bf2d59845302b55341b63e3a3f9ae7f0d98bc8d0d5a63a5"}
 
 
 def measured_record(workload, record=None, sources=None):

@@ -24,7 +24,8 @@
 //
 // Memory pipeline.  Q, dO and the (L2, -Delta) block of a step travel from
 // HBM straight into LDS (buffer loads with the LDS destination bit) two steps
-// ahead; three LDS stages, one barrier per step.  The Q/dO tiles are
+// ahead, their load instructions spread over the products of a step; four
+// LDS stages, one barrier per step.  The Q/dO tiles are
 // stored as [D/8 chunk columns][64 rows][16 bytes] with the chunk columns 64
 // bytes apart mod 256, so both fragment reads are free of bank conflicts: the
 // 16-byte reads of the score products (32 rows of one chunk column per half
@@ -68,7 +69,8 @@ struct BwdTile {
   static constexpr int QT = CH * CSTR;       // one Q or dO tile
   static constexpr int STAT = 1024;          // [L2 x 64][-Delta x 64] + landing room
   static constexpr int STAGE = 2 * QT + STAT;
-  static constexpr int LDS = 3 * STAGE;      // three stages in flight
+  static constexpr int LDS = 4 * STAGE;      // four stages in flight
+  static constexpr int NPC = 2 * CH / 4 + 1; // load instructions per wave and step
   static constexpr int NP = D / 8;           // matrix products per phase of a step
   static constexpr int LA = 6;               // operand reads run this many products ahead
 };
@@ -122,11 +124,16 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(BwdParams p, long row
 // products ahead of it, so no phase starts by draining the LDS queue, and the
 // softmax arithmetic of a block is cut into pairs of elements whose halves
 // (exponentials; products and bf16 packing) sit in slots of their own, so the
-// exponentials' latency passes while a product issues.  Three LDS stages:
-// the loads of step i+2 go to the stage step i-1 read, so the single barrier
-// of a step (before the reads of step i+1 start) waits only for loads issued
-// a step earlier and for no LDS read.
-template <int NP>
+// exponentials' latency passes while a product issues.  Four LDS stages: the
+// loads of step i+2 go to the stage step i-2 read, whose reads all completed
+// before the barrier that ended step i-1, so they can be issued anywhere in
+// step i.  One load instruction every few slots, not a burst after the
+// barrier: with one wave per SIMD a burst holds up the wave's in-order issue,
+// its matrix products included, while the CU's load path takes all four
+// waves' instructions (spreading them took 2 % off the kernel's time).  The
+// single barrier of a step (before the reads of step i+1 start) waits for
+// loads issued a step earlier and for no LDS read.
+template <int NP, int NPC, int LA>
 struct BwdSlots {
   static constexpr bool SPLIT = NP >= 16;  // pair halves in separate slots
   static constexpr int first(int b) { return SPLIT ? (b + 1) * NP + 1 + b : (b + 1) * NP + 1; }
@@ -137,7 +144,11 @@ struct BwdSlots {
   }
   // the first product that reads pair k of block b (query half k / 4)
   static constexpr int need(int b, int k) { return (2 + b) * NP + (k < 4 ? 0 : NP / 2); }
+  // slot after whose product load instruction k (0 .. NPC-1) of step i+2 is
+  // issued: spread evenly over the 4 NP - LA slots before the barrier
+  static constexpr int load_slot(int k) { return 1 + k * ((4 * NP - LA) / NPC); }
   static constexpr bool valid() {
+    if (load_slot(NPC - 1) >= 4 * NP - LA) return false;
     for (int b = 0; b < 2; ++b)
       for (int k = 0; k < 8; ++k)
         if (slot(b, k, 1) >= need(b, k) || slot(b, k, 0) < (b + 1) * NP) return false;
@@ -200,22 +211,30 @@ void attn_bwd_main_kernel(BwdParams p) {
   //      (one 1 KiB load per chunk column, lane l carrying row l; rows past S,
   //      and whole steps past the last, read as zero), then the step's
   //      (L2, -Delta) block, which every wave loads (identical bytes) so that
-  //      the issue has no wave-dependent branch.
-  static_assert(CH % NW == 0, "chunk columns must split evenly over the waves");
+  //      every wave issues the same NPC loads per step, the count the wait at
+  //      the step's barrier relies on.
+  static_assert(CH % NW == 0 && T::NPC == 2 * CH / NW + 1,
+                "chunk columns must split evenly over the waves");
+  constexpr int NPC = T::NPC;
   const int row_off = lane * (2 * D);
-  auto fetch = [&](int step, ATTN_LDS char* base) __attribute__((always_inline)) {
+  // load instruction k of a step's tiles: Q chunk columns (k < CH/NW), dO
+  // chunk columns, then the statistics block
+  auto fetch_piece = [&](int step, ATTN_LDS char* base, int k) __attribute__((always_inline)) {
     const int q0 = qfirst + step * BQ;
     const uint32_t off = (uint32_t)q0 * (2 * D);
-    const u32x4 qrs = buffer_rsrc_at(p.q + head, hbytes, off);
-    const u32x4 ors = buffer_rsrc_at(p.dout + head, hbytes, off);
-    const u32x4 srs = buffer_rsrc_at(stats_h, (uint32_t)p.nblk * 512, (uint32_t)(q0 / BQ) * 512);
-#pragma unroll
-    for (int k = 0; k < CH / NW; ++k) {
-      const int i = w + NW * k;
-      lds_dma16(base + i * CSTR, qrs, row_off, i * 16);
-      lds_dma16(base + QT + i * CSTR, ors, row_off, i * 16);
+    if (k < 2 * CH / NW) {
+      const bool isq = k < CH / NW;
+      const int i = w + NW * (isq ? k : k - CH / NW);
+      const u32x4 rs = buffer_rsrc_at(isq ? p.q + head : p.dout + head, hbytes, off);
+      lds_dma16(base + (isq ? 0 : QT) + i * CSTR, rs, row_off, i * 16);
+    } else {
+      const u32x4 srs = buffer_rsrc_at(stats_h, (uint32_t)p.nblk * 512, (uint32_t)(q0 / BQ) * 512);
+      lds_dma16(base + 2 * QT, srs, lane * 16, 0);
     }
-    lds_dma16(base + 2 * QT, srs, lane * 16, 0);
+  };
+  auto fetch = [&](int step, ATTN_LDS char* base) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < NPC; ++k) fetch_piece(step, base, k);
   };
 
   // ---- the first two steps' tiles; K and V rows of this lane's key (B
@@ -286,8 +305,9 @@ void attn_bwd_main_kernel(BwdParams p) {
       for (int e = 0; e < 4; ++e) dp[4 * g4 + e] = d[e];
     }
   };
-  // Stages rotate over three LDS slots: cur (this step), nxt (step i+1,
-  // loaded), fre (read by step i-1, receives step i+2).
+  // Stages rotate over four LDS slots: cur (this step), nxt (step i+1,
+  // loaded), fre (read by step i-2, receives step i+2 during this step), and
+  // the stage step i-1 read.
   // op holds the operands of the step's first LA products, lva/dpa block A's
   // L2 and -Delta, on entry; the next step's on exit.
   auto step = [&](auto masked_t, int i, const ATTN_LDS char* cur, const ATTN_LDS char* nxt,
@@ -352,7 +372,7 @@ void attn_bwd_main_kernel(BwdParams p) {
       pk[b][k] = pack_bf16x2(ex[b][k][0], ex[b][k][1]);
       dsk[b][k] = pack_bf16x2(ex[b][k][0] * dacc[b][2 * k], ex[b][k][1] * dacc[b][2 * k + 1]);
     };
-    using Sl = BwdSlots<NP>;
+    using Sl = BwdSlots<NP, NPC, LA>;
     static_assert(Sl::valid(), "softmax pairs must follow their scores and precede their use");
     static_assert(Sl::slot(1, 7, 1) < NX, "block B's softmax must precede the barrier");
     auto slot = [&](auto m_t) __attribute__((always_inline)) {
@@ -365,6 +385,10 @@ void attn_bwd_main_kernel(BwdParams p) {
         o[m + LA] = operand(nxt, std::integral_constant<int, m + LA - NM>{});
         if constexpr (m == NX) read_stats(nxt, 0, lva, dpa);
       }
+      static_for(std::make_integer_sequence<int, NPC>{}, [&](auto k_t) {
+        if constexpr (Sl::load_slot(decltype(k_t)::value) == m)
+          fetch_piece(i + 2, fre, decltype(k_t)::value);
+      });
       static_for(std::make_integer_sequence<int, 2>{}, [&](auto b_t) {
         static_for(std::make_integer_sequence<int, 8>{}, [&](auto k_t) {
           constexpr int b = decltype(b_t)::value, k = decltype(k_t)::value;
@@ -376,10 +400,10 @@ void attn_bwd_main_kernel(BwdParams p) {
     };
     // ---- before the barrier: products 0 .. NX-1, reads of this stage
     static_for(std::make_integer_sequence<int, NX>{}, slot);
-    // ---- step i+1's tiles have landed everywhere; stage fre is free
-    wait_vmcnt<0>();
+    // ---- step i+1's tiles have landed everywhere (loads retire in order:
+    //      only this step's NPC, for step i+2, may still be in flight)
+    wait_vmcnt<NPC>();
     barrier();
-    fetch(i + 2, fre);
     __builtin_amdgcn_sched_barrier(0);
     // ---- after the barrier: products NX .. NM-1, reads of step i+1's head
     static_for(std::make_integer_sequence<int, LA>{}, [&](auto k) {
@@ -395,13 +419,14 @@ void attn_bwd_main_kernel(BwdParams p) {
   f32x16 dpa;
   static_for(std::make_integer_sequence<int, LA>{}, [&](auto k) { op[k] = operand(lds, k); });
   read_stats(lds, 0, lva, dpa);
-  // stage rotation: offsets of cur, nxt, fre
-  int sc = 0, sn = T::STAGE, sf = 2 * T::STAGE;
+  // stage rotation: offsets of cur, nxt, fre and the stage step i-1 read
+  int sc = 0, sn = T::STAGE, sf = 2 * T::STAGE, sp = 3 * T::STAGE;
   auto rotate = [&]() {
     const int t0 = sc;
     sc = sn;
     sn = sf;
-    sf = t0;
+    sf = sp;
+    sp = t0;
   };
   int i = 0;
   if constexpr (CAUSAL) {

@@ -148,7 +148,7 @@ void attn_fwd_kernel(FwdParams p) {
   {
     const int u = blockIdx.x;
     if (p.xcd_heads > 0) {
-      const int x = u & 7, j = u >> 3, hpx = p.xcd_heads;
+      const int x = u & 7, j = u >> 3;
       if (CAUSAL) {
         // the XCD's heads in groups of xcd_group, heaviest block first
         // within a group: a group's K/V fits the XCD's L2 far better than
