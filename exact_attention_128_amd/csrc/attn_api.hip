@@ -213,7 +213,7 @@ int attn_fwd_rescale_events(const void* q, const void* k, const void* v, void* o
 size_t attn_bwd_workspace_size(int B, int H, int S, int D) {
   if (check_shape(B, H, S, D) != ATTN_OK) return 0;
   (void)D;
-  const size_t stat_bytes = size_t(B) * H * ((S + 63) / 64) * 128 * sizeof(float);
+  const size_t stat_bytes = size_t(B) * H * ((S + 63) / 64) * 64 * 16;  // 16 B per row
   return round_up(stat_bytes, 256);
 }
 
@@ -238,7 +238,7 @@ int attn_bwd_phases(const void* q, const void* k, const void* v, const void* o,
   p.dk = static_cast<uint16_t*>(dk);
   p.dv = static_cast<uint16_t*>(dv);
   p.nblk = (S + 63) / 64;
-  p.stats = static_cast<float*>(workspace);
+  p.stats = static_cast<uint16_t*>(workspace);
   p.bh = B * H;
   p.S = S;
   p.xcd_heads = (p.bh % 8 == 0) ? p.bh / 8 : 0;

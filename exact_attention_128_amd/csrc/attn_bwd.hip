@@ -11,18 +11,22 @@
 // attn_bwd_dq.hip, which owns query rows, needs no atomics and runs first: it
 // also writes the row statistics that the main kernel reads):
 //   pre    the row statistics alone, for callers that want them without dQ:
-//          per 64-row block of each head, L2_i = LSE_i * log2(e) and
-//          -Delta_i = -sum_d dO_id * O_id (fp32, from the bf16 O), zero for
-//          the padding rows past S
+//          per query row of each head, a 16-byte record of -L2_i =
+//          -LSE_i * log2(e) and -Delta_i = -sum_d dO_id * O_id (fp32 from the
+//          bf16 O, each kept as three bf16 parts; stat_record in gfx950.h),
+//          zero for the padding rows past S in the last 64-row block
 //   main   dK, dV: one workgroup per (head, 128-key block); each of its 4 waves
 //          owns 32 keys, with their K and V rows resident in registers, and
 //          walks the query blocks that can see them, 64 queries per step:
 //            S   = Q K^T,  dP = dO V^T     (keys on lanes, queries in registers)
 //            P   = exp2(S * scale*log2e - L2),  dS = P (dP - Delta)
-//          (the dP accumulator starts at -Delta, so dS is a single product)
+//          (the dP accumulator starts at -Delta, so dS is a single product;
+//          both -L2 and -Delta reach the key lanes through the matrix core:
+//          one product of the rows' statistics records against a constant
+//          0/1 operand lays each row's value across the tile)
 //            dV^T += dO^T P,  dK^T += Q^T dS   (P, dS straight from registers)
 //
-// Memory pipeline.  Q, dO and the (L2, -Delta) block of a step travel from
+// Memory pipeline.  Q, dO and the statistics records of a step travel from
 // HBM straight into LDS (buffer loads with the LDS destination bit) two steps
 // ahead, their load instructions spread over the products of a step; four
 // LDS stages, one barrier per step.  The Q/dO tiles are
@@ -67,7 +71,7 @@ struct BwdTile {
   static constexpr int KK = D / 16;          // MFMA steps over the features
   static constexpr int CSTR = BQ * 16 + 64;  // chunk column stride of a Q/dO tile
   static constexpr int QT = CH * CSTR;       // one Q or dO tile
-  static constexpr int STAT = 1024;          // [L2 x 64][-Delta x 64] + landing room
+  static constexpr int STAT = 1024;          // 64 rows x 16-byte statistics record
   static constexpr int STAGE = 2 * QT + STAT;
   static constexpr int LDS = 4 * STAGE;      // four stages in flight
   static constexpr int NPC = 2 * CH / 4 + 1; // load instructions per wave and step
@@ -103,11 +107,9 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(BwdParams p, long row
     }
 #pragma unroll
     for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-    if (c == 0) {
-      float* st = p.stats + bh * (long)per * 2 + (r / 64) * 128 + (r % 64);
-      st[0] = valid ? p.lse[row] * kLog2e : 0.0f;
-      st[64] = valid ? -acc : 0.0f;
-    }
+    if (c == 0)
+      *(u32x4*)(p.stats + (bh * (long)per + r) * 8) =
+          stat_record(valid ? -p.lse[row] * kLog2e : 0.0f, valid ? -acc : 0.0f);
   }
 }
 
@@ -202,15 +204,15 @@ void attn_bwd_main_kernel(BwdParams p) {
   const bool kvalid = key < S;
   const size_t head = (size_t)bh * S * D;
   const uint32_t hbytes = (uint32_t)S * D * 2;
-  const float* const stats_h = p.stats + (size_t)bh * p.nblk * 128;
+  const uint16_t* const stats_h = p.stats + (size_t)bh * p.nblk * 512;  // 1 KiB per 64 rows
 
   const int qfirst = CAUSAL ? k0 : 0;  // queries before k0 see none of these keys
   const int nsteps = (S - qfirst + BQ - 1) / BQ;
 
   // ---- step tiles HBM -> LDS stage: Q and dO as [chunk column][64 rows][16 B]
   //      (one 1 KiB load per chunk column, lane l carrying row l; rows past S,
-  //      and whole steps past the last, read as zero), then the step's
-  //      (L2, -Delta) block, which every wave loads (identical bytes) so that
+  //      and whole steps past the last, read as zero), then the step's 64
+  //      statistics records, which every wave loads (identical bytes) so that
   //      every wave issues the same NPC loads per step, the count the wait at
   //      the step's barrier relies on.
   static_assert(CH % NW == 0 && T::NPC == 2 * CH / NW + 1,
@@ -228,7 +230,7 @@ void attn_bwd_main_kernel(BwdParams p) {
       const u32x4 rs = buffer_rsrc_at(isq ? p.q + head : p.dout + head, hbytes, off);
       lds_dma16(base + (isq ? 0 : QT) + i * CSTR, rs, row_off, i * 16);
     } else {
-      const u32x4 srs = buffer_rsrc_at(stats_h, (uint32_t)p.nblk * 512, (uint32_t)(q0 / BQ) * 512);
+      const u32x4 srs = buffer_rsrc_at(stats_h, (uint32_t)p.nblk * 1024, (uint32_t)(q0 / BQ) * 1024);
       lds_dma16(base + 2 * QT, srs, lane * 16, 0);
     }
   };
@@ -268,6 +270,13 @@ void attn_bwd_main_kernel(BwdParams p) {
       dk[i][r] = 0.0f;
     }
   const float c = p.c;
+  // constant B operands of the statistics products: ones against the record's
+  // -L2 parts (elements 0-2) or its -Delta parts (3-5) for the lanes holding
+  // k = 0..7, zeros elsewhere (lanes 32-63 hold k = 8..15)
+  const bf16x8 ones_l2 = __builtin_bit_cast(
+      bf16x8, h == 0 ? u32x4{0x3F803F80u, 0x3F80u, 0u, 0u} : u32x4{0u, 0u, 0u, 0u});
+  const bf16x8 ones_dl = __builtin_bit_cast(
+      bf16x8, h == 0 ? u32x4{0u, 0x3F800000u, 0x3F803F80u, 0u} : u32x4{0u, 0u, 0u, 0u});
 
   // Per-lane LDS offsets (each fragment adds a constant):
   //   qa:  16-byte read of row 32sb + l32, chunk column 2kk + h
@@ -293,25 +302,19 @@ void attn_bwd_main_kernel(BwdParams p) {
       return cat_tr(lds_read_tr16(b), lds_read_tr16(b + 128));
     }
   };
-  // L2 of the block's queries 8g4 + 4h .. +3 (broadcast reads), and their
-  // -Delta as the starting value of the dP accumulator (same register order)
-  auto read_stats = [&](const ATTN_LDS char* stg, int sb, f32x4 (&lv)[4], f32x16& dp) {
-    const ATTN_LDS char* sp = stg + 2 * QT + 128 * sb + 16 * h;
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      lv[g4] = *(const ATTN_LDS f32x4*)(sp + 32 * g4);
-      const f32x4 d = *(const ATTN_LDS f32x4*)(sp + 256 + 32 * g4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) dp[4 * g4 + e] = d[e];
-    }
+  // statistics record of query 32 sb + l32 of a stage (both lane halves read
+  // the same record: the A operand of the statistics products, whose k =
+  // 8..15 half meets zeros in B but must be finite)
+  auto read_rec = [&](const ATTN_LDS char* stg, int sb) {
+    return lds_read_b128(stg + 2 * QT + (32 * sb + l32) * 16);
   };
   // Stages rotate over four LDS slots: cur (this step), nxt (step i+1,
   // loaded), fre (read by step i-2, receives step i+2 during this step), and
   // the stage step i-1 read.
-  // op holds the operands of the step's first LA products, lva/dpa block A's
-  // L2 and -Delta, on entry; the next step's on exit.
+  // op holds the operands of the step's first LA products, reca block A's
+  // statistics record, on entry; the next step's on exit.
   auto step = [&](auto masked_t, int i, const ATTN_LDS char* cur, const ATTN_LDS char* nxt,
-                  ATTN_LDS char* fre, bf16x8 (&op)[LA], f32x4 (&lva)[4], f32x16& dpa)
+                  ATTN_LDS char* fre, bf16x8 (&op)[LA], bf16x8& reca)
       __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked_t)::value;
     constexpr int STAT_B = 2;  // block B's statistics are read after this product
@@ -319,8 +322,8 @@ void attn_bwd_main_kernel(BwdParams p) {
     bf16x8 o[NM + LA];
     static_for(std::make_integer_sequence<int, LA>{}, [&](auto k) { o[k] = op[k]; });
     f32x16 sacc[2], dacc[2];
-    dacc[0] = dpa;
-    f32x4 lvb[4];
+    f32x16 nl2[2];  // -L2 of each register's query, in the score layout
+    bf16x8 recb;
     uint32_t pk[2][8], dsk[2][8];
     auto product = [&](auto m_t) __attribute__((always_inline)) {
       constexpr int m = decltype(m_t)::value, ph = m / NP, j = m % NP;
@@ -334,7 +337,21 @@ void attn_bwd_main_kernel(BwdParams p) {
           } else {
             sacc[ph] = mfma32(o[m], kf[j >> 1], sacc[ph]);
           }
+          if constexpr (j == NP - 2) {
+            // -L2 tile, late in the phase: its registers live only until
+            // the block's softmax has used them
+            f32x16 z;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) z[r] = 0.0f;
+            nl2[ph] = mfma32(ph ? recb : reca, ones_l2, z);
+          }
         } else {
+          if constexpr (j == 1) {
+            f32x16 z;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) z[r] = 0.0f;
+            dacc[ph] = mfma32(ph ? recb : reca, ones_dl, z);   // -Delta
+          }
           dacc[ph] = mfma32(o[m], vf[j >> 1], dacc[ph]);
         }
       } else {
@@ -358,11 +375,10 @@ void attn_bwd_main_kernel(BwdParams p) {
     auto half0 = [&](auto b_t, auto k_t) __attribute__((always_inline)) {
       constexpr int b = decltype(b_t)::value, k = decltype(k_t)::value, g4 = k / 2;
       const f32x16& sv = sacc[b];
-      const f32x4(&lv)[4] = b ? lvb : lva;
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         constexpr int e0 = 2 * (k % 2);
-        float v = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * k + u], c, -lv[g4][e0 + u]));
+        float v = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * k + u], c, nl2[b][2 * k + u]));
         if constexpr (MASKED) v = key <= q0 + 32 * b + 8 * g4 + 4 * h + e0 + u ? v : 0.0f;
         ex[b][k][u] = v;
       }
@@ -380,10 +396,10 @@ void attn_bwd_main_kernel(BwdParams p) {
       product(m_t);
       if constexpr (m < NX) {
         if constexpr (m + LA < NM) o[m + LA] = operand(cur, std::integral_constant<int, m + LA>{});
-        if constexpr (m == STAT_B) read_stats(cur, 1, lvb, dacc[1]);
+        if constexpr (m == STAT_B) recb = read_rec(cur, 1);
       } else {
         o[m + LA] = operand(nxt, std::integral_constant<int, m + LA - NM>{});
-        if constexpr (m == NX) read_stats(nxt, 0, lva, dpa);
+        if constexpr (m == NX) reca = read_rec(nxt, 0);
       }
       static_for(std::make_integer_sequence<int, NPC>{}, [&](auto k_t) {
         if constexpr (Sl::load_slot(decltype(k_t)::value) == m)
@@ -415,10 +431,8 @@ void attn_bwd_main_kernel(BwdParams p) {
   using Yes = std::integral_constant<bool, true>;
   using No = std::integral_constant<bool, false>;
   bf16x8 op[LA];
-  f32x4 lva[4];
-  f32x16 dpa;
   static_for(std::make_integer_sequence<int, LA>{}, [&](auto k) { op[k] = operand(lds, k); });
-  read_stats(lds, 0, lva, dpa);
+  bf16x8 reca = read_rec(lds, 0);
   // stage rotation: offsets of cur, nxt, fre and the stage step i-1 read
   int sc = 0, sn = T::STAGE, sf = 2 * T::STAGE, sp = 3 * T::STAGE;
   auto rotate = [&]() {
@@ -432,12 +446,12 @@ void attn_bwd_main_kernel(BwdParams p) {
   if constexpr (CAUSAL) {
     // keys k0 .. k0+127 against queries k0 .. k0+127: the only masked steps
     for (; i < 2 && i < nsteps; ++i) {
-      step(Yes{}, i, lds + sc, lds + sn, lds + sf, op, lva, dpa);
+      step(Yes{}, i, lds + sc, lds + sn, lds + sf, op, reca);
       rotate();
     }
   }
   for (; i < nsteps; ++i) {
-    step(No{}, i, lds + sc, lds + sn, lds + sf, op, lva, dpa);
+    step(No{}, i, lds + sc, lds + sn, lds + sf, op, reca);
     rotate();
   }
   wait_all();  // the loads of the (unused) steps past the end

@@ -107,9 +107,9 @@ void attn_bwd_dq_kernel(BwdParams p) {
   //      -inf gives P = 0) and dO as B operands (features 16kk + 8h .. +7),
   //      -LSE*log2(e) and -Delta, Delta = sum_d dO_d O_d in fp32 from the
   //      bf16 O (zero past S, which makes dS zero there).  The row statistics
-  //      also go to the workspace ([B*H][nblk][L2 x 64, -Delta x 64]), where
-  //      the dK/dV kernel reads them; rows past S inside the last 64-row
-  //      block get zeros there.
+  //      also go to the workspace, one 16-byte record per row
+  //      (stat_record), where the dK/dV kernel reads them; rows past S
+  //      inside the last 64-row block get zeros there.
   //      The loads are branch-free (a lane past S loads the last row and a
   //      mask zeroes the values), so they issue back to back in the
   //      prologue, behind the first tiles' requests.
@@ -144,11 +144,8 @@ void attn_bwd_dq_kernel(BwdParams p) {
     const float l2 = ok ? lse * kLog2e : 0.0f;
     ndl = -halfwave_sum(dsum);
     nl2 = -l2;
-    if (h == 0 && qrow < p.nblk * 64) {
-      float* st = p.stats + ((size_t)bh * p.nblk + (qrow >> 6)) * 128 + (qrow & 63);
-      st[0] = l2;
-      st[64] = ndl;
-    }
+    if (h == 0 && qrow < p.nblk * 64)
+      *(u32x4*)(p.stats + ((size_t)bh * p.nblk * 64 + qrow) * 8) = stat_record(nl2, ndl);
   };
 
   const int kend = CAUSAL ? min(S, q0 + BR) : S;

@@ -75,8 +75,9 @@ struct BwdParams {
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
-  float* stats;   // workspace [B*H][nblk][2][64] fp32: per 64-row block, LSE*log2(e)
-                  // of each row, then -Delta of each row (zero for rows past S)
+  uint16_t* stats;  // workspace [B*H][nblk * 64 rows][8] bf16: per query row the
+                    // record of -LSE*log2(e) and -Delta (stat_record in gfx950.h;
+                    // zero for the rows past S in the last 64-row block)
   int bh;
   int S;
   int nblk;       // 64-row blocks per head, ceil(S / 64)

@@ -2,8 +2,8 @@
 // allocate device memory (code under HIP graph capture, tight serving loops,
 // harnesses that forbid hipMalloc).
 //
-// The backward's only scratch space is its row-statistics workspace (per
-// 64-row block of each head, LSE*log2(e) and -Delta as fp32).  Here it lives
+// The backward's only scratch space is its row-statistics workspace (16
+// bytes per query row of each head, rounded up to 64-row blocks).  Here it lives
 // in a file-scope device array of kScratchBytes, one copy per GPU, held until
 // the process ends.  The array's host-side name is a stand-in, not a device
 // address: the device address comes from hipGetSymbolAddress, fetched once per
@@ -25,7 +25,7 @@
 
 namespace {
 
-constexpr size_t kScratchBytes = size_t(16) << 20;   // 16 MiB per GPU
+constexpr size_t kScratchBytes = size_t(32) << 20;   // 32 MiB per GPU
 constexpr int kMaxDevices = 64;
 
 static __device__ __align__(256) char scratch[kScratchBytes];

@@ -37,6 +37,21 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, p);
 }
 
+// The backward's row-statistics record, 16 bytes per query row: a and b
+// (-LSE*log2(e) and -Delta) each as the sum of three bf16 parts, hi + mid +
+// lo, then two zero parts: [a0 a1 a2 b0 b1 b2 0 0].  Each part is the
+// round-to-nearest-even bf16 of what the earlier parts leave (the
+// differences are exact in fp32), so the three reproduce the value to about
+// 2^-26 relative.  The dK/dV kernel feeds the record to the matrix core as
+// an A operand against constant 0/1 B operands, which adds the parts back in
+// fp32 and lays one row's value across every key lane of the output tile.
+__device__ __forceinline__ u32x4 stat_record(float a, float b) {
+  auto bf = [](float x) { return __uint_as_float(pack_bf16x2(x, 0.0f) << 16); };
+  const float a0 = bf(a), a1 = bf(a - a0), a2 = (a - a0) - a1;
+  const float b0 = bf(b), b1 = bf(b - b0), b2 = (b - b0) - b1;
+  return u32x4{pack_bf16x2(a0, a1), pack_bf16x2(a2, b0), pack_bf16x2(b1, b2), 0u};
+}
+
 // Value held by the lane in the other half of the wave (lane ^ 32), combined.
 __device__ __forceinline__ float halfwave_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);

@@ -197,9 +197,10 @@ int attn_fwd_rescale_events(const void* q, const void* k, const void* v, void* o
 
 /*
  * Bytes of device workspace attn_bwd needs for this shape (0 if the shape is
- * invalid): two fp32 row statistics per query row, LSE_i * log2(e) and
- * -Delta_i = -sum_d dO_id * O_id, stored per 64-row block ([B][H][ceil(S/64)]
- * [2][64]), rounded up to 256 bytes.  A convention of this library, not of
+ * invalid): a 16-byte record of two row statistics per query row,
+ * -LSE_i * log2(e) and -Delta_i = -sum_d dO_id * O_id, each as three bf16
+ * parts that sum to it in fp32 ([B][H][64 * ceil(S/64)][8] bf16, i.e. 1 KiB
+ * per 64-row block), rounded up to 256 bytes.  A convention of this library, not of
  * the pages, which describe no interface: the caller owns every buffer, so
  * the backward's scratch space is passed in.  (The statistics themselves are
  * the backward's row sums Delta_i and the recomputation from LSE that the
@@ -254,7 +255,7 @@ int attn_bwd_phases(const void* q, const void* k, const void* v, const void* o,
  * cannot allocate device memory (code under HIP graph capture, tight serving
  * loops, harnesses that forbid hipMalloc).  Computes exactly what attn_bwd
  * computes, with the same kernels, bit for bit; the workspace is a static
- * device array of attn_noalloc_scratch_bytes() (16 MiB) inside the library,
+ * device array of attn_noalloc_scratch_bytes() (32 MiB) inside the library,
  * one per GPU, held until the process ends.  The call makes no hipMalloc,
  * hipFree or other allocating call (its first call on a device looks up that
  * device's copy of the array with hipGetSymbolAddress).

@@ -129,7 +129,7 @@ int main(void) {
   CHECK(attn_fwd_default_policy(128, 1, 8192, 0, &poly), 1);
   CHECK(attn_fwd_rescale_events(P, P, P, P, F, 1, 1, 300, 128, 0.1f, 1, 8.0f, 0, 0), 1);
   CHECK(attn_fwd_fp8(P, P, P, P, F, 1, 1, 300, 128, 1e30f, 1, 1e30f, 1.0f, 1.0f, 0), 6);
-  CHECK(attn_bwd_phases(P, P, P, P, F, P, P, P, P, P, 512, 1, 1, 16, 128, 0.1f, 1, 8, 0), 7);
+  CHECK(attn_bwd_phases(P, P, P, P, F, P, P, P, P, P, 1024, 1, 1, 16, 128, 0.1f, 1, 8, 0), 7);
   CHECK(attn_bwd(P, P, P, P, F, P, P, P, P, P, 511, 1, 1, 16, 128, 0.1f, 1, 0), 5);
   CHECK(attn_bwd_noalloc(P, P, P, P, F, P, P, P, P, 1, 32, 65537, 128, 0.1f, 1, 0), 9);
   CHECK(attn_bwd_noalloc(0, P, P, P, F, P, P, P, P, 1, 1, 16, 128, 0.1f, 1, 0), 1);
@@ -146,7 +146,7 @@ int main(void) {
   CHECK(attn_fwd_rescale_events(P, P, P, P, F, 1, 1, 300, 128, 0.1f, 1, 8.0f, (unsigned long long*)P, 0), 0);
   CHECK(attn_fwd_fp8(P, P, P, P, F, 1, 1, 300, 128, 0.1f, 1, 0.5f, 0.25f, 2.0f, 0), 0);
   CHECK(attn_bwd(P, P, P, P, F, P, P, P, P, P, attn_bwd_workspace_size(1, 1, 300, 128), 1, 1, 300, 128, 0.1f, 1, 0), 0);
-  CHECK(attn_bwd_phases(P, P, P, P, F, P, P, P, P, P, 4096, 1, 1, 300, 128, 0.1f, 0, 3, 0), 0);
+  CHECK(attn_bwd_phases(P, P, P, P, F, P, P, P, P, P, 8192, 1, 1, 300, 128, 0.1f, 0, 3, 0), 0);
   CHECK(stub_launches() - before, 8);
   puts("abi ok");
   return 0;

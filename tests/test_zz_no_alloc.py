@@ -16,9 +16,10 @@ def test_scratch_limit_rejected_on_the_host():
     import exact_attention_128_amd as A
     lib = A.load()
     cap = lib.attn_noalloc_scratch_bytes()
-    assert cap == 16 << 20
+    assert cap == 32 << 20
     Pp = 0x10000  # fake, aligned: never dereferenced (rejected before any HIP call)
-    # 32768 blocks of 64 rows fill the array exactly; one more row block is too many
+    # 32768 blocks of 64 rows (1 KiB each) fill the array exactly; one more row
+    # block is too many
     B, H, D = 1, 32, 128
     for S, want in ((65536 + 1, 9), (1 << 20, 9)):
         assert lib.attn_bwd_workspace_size(B, H, S, D) > cap
