@@ -65,18 +65,18 @@ TRAFFIC_SOURCES = ("exact_attention_128_amd/csrc/attn_bwd.hip",
                    "exact_attention_128_amd/csrc/gfx950.h",
                    "exact_attention_128_amd/csrc/attn_internal.h",
                    "exact_attention_128_amd/build.py")
-TRAFFIC = {"workload": "bwd_causal_s4k", "read_bytes": 231122800, "write_bytes": 67108864,
-           "cycles": 513420,
-           "sources_sha256": "f5c3e9878cf68e6bffb25d140d34738ec91b7e2b4844818e28f81b540d4e5c96"}
+TRAFFIC = {"workload": "bwd_causal_s4k", "read_bytes": 233957580, "write_bytes": 67113440,
+           "cycles": 504593,
+           "sources_sha256": "1540a5218b361e2ab344bb64542c8011e1eab141efb374c974ae2067bc99a1bf"}
 # the same for the forward on the causal S=8192 workload
 # (profiles/fwd_causal_s8k_counters.md)
 FWD_TRAFFIC_SOURCES = ("exact_attention_128_amd/csrc/attn_fwd.hip",
                        "exact_attention_128_amd/csrc/gfx950.h",
                        "exact_attention_128_amd/csrc/attn_internal.h",
                        "exact_attention_128_amd/build.py")
-FWD_TRAFFIC = {"workload": "fwd_causal_s8k", "read_bytes": 582236146, "write_bytes": 136314880,
-               "cycles": 1785060,
-               "sources_sha256": "412e51c456aef46b77c96fbc56224be43a66320f04cbf535c1603f18e24d3cc1"}
+FWD_TRAFFIC = {"workload": "fwd_causal_s8k", "read_bytes": 573210646, "write_bytes": 136314880,
+               "cycles": 1802594,
+               "sources_sha256": "04b8d82e74ca743e22d3304474d589e61fa4d7834585f6d7b917324d90d93470"}
 # the wall cycles of the step's three kernels on the causal S=4096 workload
 # (forward, dQ, dK/dV; profiles/bwd_causal_s4k_counters.md): the step's work
 # per cycle, whatever clock the power limit leaves it
@@ -86,8 +86,8 @@ STEP_SOURCES = ("exact_attention_128_amd/csrc/attn_fwd.hip",
                 "exact_attention_128_amd/csrc/gfx950.h",
                 "exact_attention_128_amd/csrc/attn_internal.h",
                 "exact_attention_128_amd/build.py")
-STEP_CYCLES = {"workload": "bwd_causal_s4k", "cycles": 284524 + 349565 + 513420,
-               "sources_sha256": "d0522020f0e5917d7bf2d59845302b55341b63e3a3f9ae7f0d98bc8d0d5a63a5"}
+STEP_CYCLES = {"workload": "bwd_causal_s4k", "cycles": 287818 + 361198 + 504593,
+               "sources_sha256": "63da3fc413eac7ede7f5a4aeb5b38d86b726f034ef86ea334a8b68ac3245a16a"}
 
 
 def measured_record(workload, record=None, sources=None):
@@ -291,10 +291,10 @@ def _alg_bytes(fam, w):
     """(read, write) algorithmic HBM bytes of one launch of kernel family fam
     on workload w: each input read once and each output written once (bf16
     tensors, E4M3 codes for the FP8 forward's inputs, fp32 LSE and the
-    backward's per-64-row statistics)."""
+    backward's 16-byte statistics record per row, in 64-row blocks)."""
     T = w.B * w.H * w.S * w.D * 2
     L = w.B * w.H * w.S * 4
-    ST = w.B * w.H * (-(-w.S // 64)) * 512
+    ST = w.B * w.H * (-(-w.S // 64)) * 1024
     return {"attn_fwd_kernel": (3 * T, T + L), "attn_fwd_short_kernel": (3 * T, T + L),
             "attn_fwd_fp8_kernel": (3 * T // 2, T + L),
             "attn_bwd_dq_kernel": (5 * T + L, T + ST), "attn_bwd_main_kernel": (4 * T + ST, 2 * T),
