@@ -229,7 +229,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o,
 
 /* Phases of the backward, for attn_bwd_phases. */
 enum attn_bwd_phase {
-  ATTN_BWD_PRE = 1,   /* LSE*log2(e) and -Delta = -rowsum(dO * O) into the workspace */
+  ATTN_BWD_PRE = 1,   /* -LSE*log2(e), -Delta = -rowsum(dO * O) records into the workspace */
   ATTN_BWD_MAIN = 2,  /* dK, dV written (reads the workspace)                      */
   ATTN_BWD_DQ = 4,    /* dQ written; writes the same statistics as PRE             */
   ATTN_BWD_ALL = 7

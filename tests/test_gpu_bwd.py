@@ -260,3 +260,51 @@ def test_full_size_workload():
         P.assert_grads_ok(err, "head %d" % hd)
     colsum = np.abs(got[1].sum(axis=2)).max()
     assert colsum <= 1.0, "sum_j dK_j far from zero: %.3e" % colsum
+
+
+@pytest.mark.parametrize("phase", ["PRE", "DQ"])
+def test_statistics_records(phase):
+    """The workspace the dK/dV kernel reads, as both writers leave it (the
+    statistics kernel, PRE, and the dQ kernel, DQ): per query row a record of
+    three bf16 parts of -LSE*log2(e), three of -Delta, two zeros.  The first
+    three parts summed in fp64 and rounded once to fp32 must give back exactly
+    the fp32 -LSE*log2(e) (each part is the bf16 rounding of what the earlier
+    ones leave, so the rest is below half an fp32 ulp), each part must be
+    within half a bf16 ulp of what the earlier ones leave, -Delta must match
+    -sum_d dO*O (fp64 on the same bf16 values), and the padding rows of the
+    last 64-row block must be all zero."""
+    import torch
+    import exact_attention_128_amd as A
+    B, H, S, D = 2, 3, 300, 128   # 5 blocks of 64 rows, 20 padding rows
+    bits = ai.make_inputs(B, H, S, D, 47, with_dout=True)
+    dev = torch.device("cuda", 0)
+    q, k, v, do = (ai.to_torch_bf16(bits[n], dev) for n in ("q", "k", "v", "do"))
+    o, lse = A.fwd(q, k, v, causal=True, scale=1.0 / np.sqrt(D))
+    n = A.bwd_workspace_size(B, H, S, D)
+    ws = torch.full((n,), 0x7f, dtype=torch.uint8, device=dev)   # garbage
+    outs = [torch.empty_like(q) for _ in range(3)]
+    ph = A.BWD_PRE if phase == "PRE" else A.BWD_DQ
+    A.bwd_out(q, k, v, o, lse, do, *outs, ws, causal=True, scale=1.0 / np.sqrt(D), phases=ph)
+    torch.cuda.synchronize()
+    nrows = 64 * ((S + 63) // 64)
+    rec = ws.cpu().numpy()[:B * H * nrows * 16].view(np.uint16).reshape(B * H, nrows, 8)
+    parts = ai.bf16_bits_to_f64(rec)
+    assert np.all(parts[:, S:, :] == 0), "padding rows must be zero"
+    assert np.all(rec[:, :, 6:] == 0)
+    valid = parts[:, :S, :]
+    want_l = (-lse.cpu().numpy().reshape(B * H, S).astype(np.float32)
+              * np.float32(1.4426950408889634)).astype(np.float32)
+    got_l = (valid[:, :, 0] + valid[:, :, 1] + valid[:, :, 2]).astype(np.float32)
+    assert np.array_equal(got_l, want_l), "-LSE*log2(e) not reproduced exactly"
+    for j in (0, 3):   # the parts: each the bf16 rounding of what the earlier ones leave
+        x = valid[:, :, j] + valid[:, :, j + 1] + valid[:, :, j + 2]
+        r1 = x - valid[:, :, j]
+        assert np.all(np.abs(r1) <= 2.0 ** -8 * np.abs(x) + 1e-300)
+        r2 = r1 - valid[:, :, j + 1]
+        assert np.all(np.abs(r2) <= 2.0 ** -8 * np.abs(r1) + 1e-300)
+    o64 = ai.bf16_bits_to_f64(ai.torch_bf16_to_bits(o)).reshape(B * H, S, D)
+    do64 = ai.bf16_bits_to_f64(bits["do"]).reshape(B * H, S, D)
+    want_d = -(o64 * do64).sum(axis=2)
+    got_d = valid[:, :, 3] + valid[:, :, 4] + valid[:, :, 5]
+    scale_d = (np.abs(o64 * do64)).sum(axis=2) + 1e-30
+    assert np.max(np.abs(got_d - want_d) / scale_d) < 1e-6, "-Delta off"
