@@ -27,9 +27,9 @@
 // 464 up into NaN), and weights down to 2^-10 relative to the offset survive
 // as subnormals.  O is normalised by the sum of the E4M3-rounded weights the
 // PV product consumes, l^ -- computed by the matrix core itself, one product
-// per 64 keys with an all-ones A operand (in this kernel the softmax, not the
-// matrix core, sets the pace, so the matrix core has room) -- and the LSE by
-// the fp32 sum of the unrounded weights.
+// per 64 keys with an all-ones A operand (the matrix core has room here: a
+// step's 18 FP8 products take about half the matrix time of the bf16
+// kernel's 64) -- and the LSE by the fp32 sum of the unrounded weights.
 //
 // Work decomposition, LDS rings, load placement and the two-wave ping-pong
 // per SIMD are those of the bf16 kernel (attn_fwd.hip); K and V tiles are
