@@ -89,6 +89,7 @@ hipError_t launch_fwd_fp8(const Fp8FwdParams& p, int, bool, hipStream_t) {
 }
 }
 extern "C" int stub_launches(void) { return attn::g_launches; }
+extern "C" int stub_xcd_group(int hpx, long kv_bytes) { return attn::xcd_group(hpx, kv_bytes); }
 """
 
 ABI_DRIVER = r"""
@@ -97,6 +98,7 @@ ABI_DRIVER = r"""
 #include <stdio.h>
 #include "attn.h"
 int stub_launches(void);
+int stub_xcd_group(int hpx, long kv_bytes);
 #define P ((void*)(uintptr_t)0x10000)
 #define F ((float*)(uintptr_t)0x10000)
 #define CHECK(expr, want) do { int r_ = (expr); if (r_ != (want)) { \
@@ -148,6 +150,18 @@ int main(void) {
   CHECK(attn_bwd(P, P, P, P, F, P, P, P, P, P, attn_bwd_workspace_size(1, 1, 300, 128), 1, 1, 300, 128, 0.1f, 1, 0), 0);
   CHECK(attn_bwd_phases(P, P, P, P, F, P, P, P, P, P, 8192, 1, 1, 300, 128, 0.1f, 0, 3, 0), 0);
   CHECK(stub_launches() - before, 8);
+  /* causal head groups per XCD: the largest divisor of the XCD's heads whose
+     K/V fits 8 MiB, at least two (or all heads when no such divisor exists) */
+  const long MiB = 1L << 20;
+  CHECK(stub_xcd_group(0, MiB), 1);
+  CHECK(stub_xcd_group(1, 64 * MiB), 1);
+  CHECK(stub_xcd_group(2, 64 * MiB), 2);
+  CHECK(stub_xcd_group(4, 2 * MiB), 4);    /* bf16, S = 4096, 32 heads */
+  CHECK(stub_xcd_group(8, 4 * MiB), 2);    /* bf16, S = 8192, 64 heads */
+  CHECK(stub_xcd_group(8, 2 * MiB), 4);    /* E4M3, S = 8192, 64 heads */
+  CHECK(stub_xcd_group(12, MiB), 6);
+  CHECK(stub_xcd_group(9, 4 * MiB), 9);    /* no divisor fits: all at once */
+  CHECK(stub_xcd_group(6, 8 * MiB), 2);
   puts("abi ok");
   return 0;
 }
