@@ -73,15 +73,17 @@ void attn_bwd_dq_kernel(BwdParams p) {
   const int S = p.S;
 
   // ---- work unit: (head, 256-row query block), heaviest first under the
-  //      causal mask; XCD-aware order as in the forward.
+  //      causal mask; XCD-aware order as in the forward (causal: the XCD's
+  //      heads xcd_group at a time, heaviest block first within a group).
   int bh, qi;
   {
     const int u = blockIdx.x;
     if (p.xcd_heads > 0) {
-      const int x = u & 7, j = u >> 3, hpx = p.xcd_heads;
+      const int x = u & 7, j = u >> 3;
       if (CAUSAL) {
-        qi = j / hpx;
-        bh = x + 8 * (j % hpx);
+        const int G = p.xcd_group, per = G * p.nqb, gi = j / per, r = j % per;
+        qi = r / G;
+        bh = x + 8 * (gi * G + r % G);
       } else {
         bh = x + 8 * (j / p.nqb);
         qi = j % p.nqb;
@@ -378,6 +380,7 @@ static hipError_t launch_dq_t(const BwdParams& p0, hipStream_t stream) {
   constexpr int NW = 8;
   BwdParams p = p0;
   p.nqb = (p.S + 32 * NW - 1) / (32 * NW);
+  p.xcd_group = xcd_group(p.xcd_heads, 4L * p.S * D);   // bf16 K and V of a head
   const long grid = (long)p.bh * p.nqb;
   if (grid <= 0 || grid * NW * 64 > 0xffffffffL) return hipErrorInvalidConfiguration;
   void* args[] = {&p};

@@ -89,6 +89,8 @@ struct BwdParams {
   uint32_t qxor;  //   applied to every Q word pair: 0, or 0x80008000 when scale < 0
   uint32_t qand;  //   0xffffffff, or 0 when scale == 0 (Q' = 0)
   int xcd_heads;  // heads per XCD for the XCD-aware block order, 0 = plain order
+  int xcd_group;  // dQ kernel, causal: an XCD works through its heads this many
+                  // at a time (set by its launcher; the dK/dV kernel takes all)
 };
 
 // ATTN_OK for hipSuccess; otherwise records e as the calling thread's last HIP

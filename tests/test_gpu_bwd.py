@@ -308,3 +308,37 @@ def test_statistics_records(phase):
     got_d = valid[:, :, 3] + valid[:, :, 4] + valid[:, :, 5]
     scale_d = (np.abs(o64 * do64)).sum(axis=2) + 1e-30
     assert np.max(np.abs(got_d - want_d) / scale_d) < 1e-6, "-Delta off"
+
+
+@pytest.mark.parametrize("shape", [(1, 48, 4096, 128), (1, 64, 8192, 64)])
+def test_causal_dq_head_groups(shape):
+    """The dQ kernel's causal XCD order in K/V-sized head groups (6 heads per
+    XCD in groups of 3; 8 per XCD in groups of 4 at D = 64).  A work unit
+    reads and writes the rows of the head it is given, so an order that
+    computed some (head, query block) twice would leave another never
+    computed: dQ starts as NaN and must come out finite everywhere.  The last
+    200 query rows of a few heads are checked against the oracle."""
+    import torch
+    import exact_attention_128_amd as A
+    B, H, S, D = shape
+    bits = ai.make_inputs(B, H, S, D, 4700 + H + D, with_dout=True)
+    scale = 1.0 / np.sqrt(D)
+    dev = torch.device("cuda", 0)
+    q, k, v, do = (ai.to_torch_bf16(bits[n], dev) for n in ("q", "k", "v", "do"))
+    o, lse = A.fwd(q, k, v, causal=True, scale=scale)
+    ws = torch.empty(A.bwd_workspace_size(B, H, S, D), dtype=torch.uint8, device=dev)
+    dq = torch.full_like(q, float("nan"))
+    dk, dv = torch.empty_like(q), torch.empty_like(q)
+    A.bwd_out(q, k, v, o, lse, do, dq, dk, dv, ws, causal=True, scale=scale, phases=A.BWD_DQ)
+    torch.cuda.synchronize()
+    got = ai.bf16_bits_to_f64(ai.torch_bf16_to_bits(dq))
+    assert np.all(np.isfinite(got)), "a (head, query block) of dQ was never computed"
+    n = 200
+    f64 = {nm: ai.bf16_bits_to_f64(bits[nm]) for nm in ("q", "k", "v", "do")}
+    for hd in (0, 7, 8, B * H - 1):
+        b, h = divmod(hd, H)
+        ref = oracle.attn_bwd_causal_tail(f64["q"][b, h, S - n:], f64["do"][b, h, S - n:],
+                                          f64["k"][b, h], f64["v"][b, h], scale)[0]
+        err = float(np.abs(got[b, h, S - n:] - ref).max())
+        print(shape, "head", hd, "dQ tail max err %.3e" % err)
+        assert err <= 5e-2, "head %d dQ tail error %.3e" % (hd, err)
