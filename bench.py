@@ -65,18 +65,18 @@ TRAFFIC_SOURCES = ("exact_attention_128_amd/csrc/attn_bwd.hip",
                    "exact_attention_128_amd/csrc/gfx950.h",
                    "exact_attention_128_amd/csrc/attn_internal.h",
                    "exact_attention_128_amd/build.py")
-TRAFFIC = {"workload": "bwd_causal_s4k", "read_bytes": 233957580, "write_bytes": 67113440,
-           "cycles": 504593,
-           "sources_sha256": "1540a5218b361e2ab344bb64542c8011e1eab141efb374c974ae2067bc99a1bf"}
+TRAFFIC = {"workload": "bwd_causal_s4k", "read_bytes": 235468705, "write_bytes": 67109173,
+           "cycles": 500167,
+           "sources_sha256": "9dcb570e1ffcbc2176f3a0c46d72955a4cca3efeb5e094b63396ef7d16258764"}
 # the same for the forward on the causal S=8192 workload
 # (profiles/fwd_causal_s8k_counters.md)
 FWD_TRAFFIC_SOURCES = ("exact_attention_128_amd/csrc/attn_fwd.hip",
                        "exact_attention_128_amd/csrc/gfx950.h",
                        "exact_attention_128_amd/csrc/attn_internal.h",
                        "exact_attention_128_amd/build.py")
-FWD_TRAFFIC = {"workload": "fwd_causal_s8k", "read_bytes": 573210646, "write_bytes": 136314880,
-               "cycles": 1802594,
-               "sources_sha256": "04b8d82e74ca743e22d3304474d589e61fa4d7834585f6d7b917324d90d93470"}
+FWD_TRAFFIC = {"workload": "fwd_causal_s8k", "read_bytes": 582272535, "write_bytes": 136314880,
+               "cycles": 1782431,
+               "sources_sha256": "1d7cf01eed59945fef8688b54fc5bc3d679d5caeba268231974cc68888b113e1"}
 # the wall cycles of the step's three kernels on the causal S=4096 workload
 # (forward, dQ, dK/dV; profiles/bwd_causal_s4k_counters.md): the step's work
 # per cycle, whatever clock the power limit leaves it
@@ -86,8 +86,8 @@ STEP_SOURCES = ("exact_attention_128_amd/csrc/attn_fwd.hip",
                 "exact_attention_128_amd/csrc/gfx950.h",
                 "exact_attention_128_amd/csrc/attn_internal.h",
                 "exact_attention_128_amd/build.py")
-STEP_CYCLES = {"workload": "bwd_causal_s4k", "cycles": 287818 + 361198 + 504593,
-               "sources_sha256": "63da3fc413eac7ede7f5a4aeb5b38d86b726f034ef86ea334a8b68ac3245a16a"}
+STEP_CYCLES = {"workload": "bwd_causal_s4k", "cycles": 285341 + 355852 + 500167,
+               "sources_sha256": "3a9824d80ddbaa143b42e9ad0f7db1b2e174c7d7e587832bf01093972d045d70"}
 
 
 def measured_record(workload, record=None, sources=None):
