@@ -67,6 +67,24 @@ def test_full_size_workload_sampled_rows():
     P.check_fp8(bits, w.causal, w.scale, rows_by_head=rows, what="fp8 full size")
 
 
+def test_full_size_every_unit_written():
+    """The same workload with O and LSE starting as NaN: every (head, query
+    block) unit of the causal XCD order (heads in groups of four per XCD at
+    this size) writes its rows, so nothing stays NaN."""
+    import torch
+    import exact_attention_128_amd as A
+    w = ai.FP8_WORKLOAD
+    b8 = ai.make_inputs_fp8(w.B, w.H, w.S, w.D, w.seed)
+    dev = torch.device("cuda", 0)
+    q, k, v = (ai.to_torch_u8(b8[n], dev) for n in ("q", "k", "v"))
+    o = torch.full(q.shape, float("nan"), dtype=torch.bfloat16, device=dev)
+    lse = torch.full((w.B, w.H, w.S), float("nan"), dtype=torch.float32, device=dev)
+    A.fwd_fp8_out(q, k, v, b8["q_descale"], b8["k_descale"], b8["v_descale"], o, lse,
+                  causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o.float()).all()) and bool(torch.isfinite(lse).all())
+
+
 def test_matrix_core_accumulation_bound():
     """S = 1: the LSE is the single score itself, so its error is the FP8
     matrix core's dot-product error, checked against the contract's
