@@ -22,13 +22,16 @@
  *     ((b*H + h)*S + i)*D + d.  Q, K, V, O, dO, dQ, dK, dV are bf16 (16-bit
  *     brain float, passed as raw 16-bit words); LSE is fp32 [B][H][S].
  *   - All tensor pointers are DEVICE pointers on the current HIP device, owned
- *     by the caller.  The library allocates no device memory and keeps no device
- *     state; the backward's scratch space is a caller-provided workspace.
+ *     by the caller.  The library allocates no device memory when called; the
+ *     backward's scratch space is a caller-provided workspace (attn_bwd_noalloc
+ *     instead uses a fixed array inside the library, described there).
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
  *     the call returns without synchronising.  Errors raised while the kernels
  *     run surface at the caller's next synchronisation on that stream.
  *   - Arguments are validated on the host before any HIP call.  No C++
- *     exception crosses this boundary.  Calls are thread-safe and re-entrant.
+ *     exception crosses this boundary.  Calls are thread-safe and re-entrant
+ *     (attn_bwd_noalloc calls that overlap on one GPU share its array: see
+ *     there).
  *   - Supported: B, H, S >= 1 (any S; partial tiles are masked), D in {64, 128},
  *     B*H*S*D < 2^40 elements, S*D < 2^29, and B*H*ceil(S/256) < 2^23 (the
  *     kernels run one workgroup per 256-row block on a one-dimensional grid,
